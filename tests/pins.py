@@ -1,0 +1,475 @@
+"""Pins for the CPU oracle: checks against facts that do not come from the
+oracle itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with what the pages or the mathematics fix:
+
+* worked quantization examples (tests/golden/quantize_ties.txt) and a brute
+  force "nearest code, ties away from zero" search over all 255 codes;
+* cache layouts re-derived with numpy transposes;
+* the integer QK accumulator recomputed with numpy int64 dot products, the
+  score chain checked against fp64;
+* the softmax probabilities against an fp64 softmax of the same scores;
+* W-group quantization against the brute-force nearest code on aligned
+  groups; ranges and int32 bounds;
+* the output re-assembled from the intermediates (the error decomposition of
+  the page "Implementing INT8 PV MMAC on a gfx936 DCU", section 1);
+* partition / tile invariance: exact fp64 attention over the dequantized cache
+  computed by numpy must equal the oracle's partitioned or tiled result;
+* brute force against unquantized fp64 attention within an a-priori bound;
+* special cases with closed-form answers (one token, equal scores, one
+  dominant score, empty sequence).
+
+The mutation tests run the same functions on oracle builds with planted
+mistakes and require at least one pin to fail for each.
+"""
+from __future__ import annotations
+
+from pathlib import Path
+
+import numpy as np
+
+import workloads as W
+from oracle import ORC_EXACT, ORC_NO_WQUANT
+from refmath import (cache_rows, decode_reference_fp64, prefill_reference_fp64,
+                     seq_slots)
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+CODES = np.arange(-127, 128, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+def nearest_code(r: np.ndarray) -> np.ndarray:
+    """Brute force: the code in [-127, 127] nearest to each r; ties go to the
+    code of larger magnitude (half away from zero)."""
+    r = np.asarray(r, np.float64).reshape(-1)
+    dist = np.abs(r[:, None] - CODES[None, :].astype(np.float64))
+    best = dist.min(axis=1, keepdims=True)
+    cand = np.where(dist == best, np.abs(CODES)[None, :], -1)
+    pick = cand.argmax(axis=1)
+    return CODES[pick]
+
+
+def check_group_quant(w: np.ndarray, wq: np.ndarray, sw: np.float32, where: str):
+    """sW = max W / 127 (fp32) and Wq = nearest code of W / sW (fp32)."""
+    w = np.asarray(w, np.float32)
+    amax = np.float32(np.abs(w).max()) if w.size else np.float32(0)
+    if amax == 0:
+        assert sw == 0 and not wq.any(), f"{where}: zero group must give sW=0, Wq=0"
+        return
+    exp_sw = np.float32(amax) / np.float32(127)
+    assert np.float32(sw).view(np.uint32) == exp_sw.view(np.uint32), \
+        f"{where}: sW {sw!r} != max/127 {exp_sw!r}"
+    r = (w / np.float32(sw)).astype(np.float32)
+    exp_q = nearest_code(r)
+    assert np.array_equal(wq.astype(np.int64), exp_q), f"{where}: Wq differs from nearest code"
+    assert wq.min() >= 0 and wq.max() <= 127, f"{where}: Wq outside [0,127]"
+    assert wq.max() == 127, f"{where}: nonzero group without a 127 code"
+
+
+def tiny_decode(seed=5, seq_lens=(1, 5, 16, 17, 80, 256, 257, 300, 700), Hq=4, Hkv=2,
+                D=32, **kw):
+    return W.make_workload("tiny_decode", seq_lens=list(seq_lens),
+                           new_tokens=[1] * len(seq_lens), num_q_heads=Hq,
+                           num_kv_heads=Hkv, head_dim=D, seed=seed, **kw)
+
+
+def tiny_prefill(seed=9, seq_lens=(40, 300, 33, 130), new=(8, 50, 33, 1), Hq=4, Hkv=2,
+                 D=32, **kw):
+    return W.make_workload("tiny_prefill", seq_lens=list(seq_lens), new_tokens=list(new),
+                           num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, seed=seed,
+                           kind="prefill", **kw)
+
+
+# ---------------------------------------------------------------------------
+# quantization
+# ---------------------------------------------------------------------------
+def pin_quantize_golden(orc):
+    n = 0
+    for line in (GOLDEN / "quantize_ties.txt").read_text().splitlines():
+        if not line.strip() or line.startswith("#"):
+            continue
+        xs, s, qs = (part.split() for part in line.split("|"))
+        x = np.array([float(v) for v in xs], np.float32)
+        assert np.array_equal(W.bf16_bits_to_f32(W.f32_to_bf16_bits(x)), x)
+        q, sc = orc.quantize(x)
+        assert sc == np.float32(float(s[0])), f"golden scale {sc} != {s[0]}"
+        assert np.array_equal(q.astype(int), np.array([int(v) for v in qs])), \
+            f"golden codes {q.tolist()} != {qs}"
+        n += 1
+    assert n >= 5
+
+
+def pin_quantize_bruteforce(orc, n_vec=240, seed=11):
+    rng = np.random.default_rng(seed)
+    for t in range(n_vec):
+        D = int(rng.choice([16, 128, 256]))
+        kind = t % 4
+        if kind == 0:
+            x = rng.standard_normal(D).astype(np.float32)
+        elif kind == 1:     # exact ties: (k + 1/2) * 2^e with one element at 127 * 2^e
+            e = float(2.0 ** rng.integers(-20, 20))
+            k = rng.integers(-126, 127, D).astype(np.float64) + 0.5 * rng.integers(0, 2, D)
+            k[rng.integers(D)] = 127.0 * (1 if rng.random() < 0.5 else -1)
+            x = (k * e).astype(np.float32)
+        elif kind == 2:     # tiny magnitudes: scales fall into the subnormal range
+            x = (rng.standard_normal(D) * 1e-38).astype(np.float32)
+        else:               # wide dynamic range
+            x = (rng.standard_normal(D) * 10.0 ** rng.uniform(-30, 30, D)).astype(np.float32)
+        x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x))
+        q, s = orc.quantize(x)
+        amax = np.float32(np.abs(x).max())
+        if amax == 0:
+            assert s == 0 and not q.any()
+            continue
+        exp_s = amax / np.float32(127)
+        assert s.view(np.uint32) == exp_s.view(np.uint32), "scale must be amax/127 in fp32"
+        r = (x / s).astype(np.float32)
+        assert np.array_equal(q.astype(np.int64), nearest_code(r)), "codes not nearest/ties-away"
+        assert abs(int(q[np.argmax(np.abs(x))])) == 127
+        assert q.min() >= -127
+        err = np.abs(q.astype(np.float64) * s - x.astype(np.float64))
+        assert np.all(err <= s * (0.5 + 1e-5)), "dequantization error above half a step"
+
+
+# ---------------------------------------------------------------------------
+# producer / layout
+# ---------------------------------------------------------------------------
+def pin_cache_layout(orc):
+    wl = W.make_workload("layout", seq_lens=[37, 16, 1, 70], new_tokens=[1] * 4,
+                         num_q_heads=4, num_kv_heads=2, head_dim=64, seed=21)
+    rng = np.random.default_rng(3)
+    T = wl.num_tokens
+    slots = wl.slot_mapping.copy()
+    skip = rng.choice(T, 6, replace=False)
+    slots[skip] = -1
+    qry = W.f32_to_bf16_bits(rng.standard_normal((T, 4, 64), dtype=np.float32))
+    cache = orc.empty_cache(wl.num_blocks, 2, 64)
+    q8, qs = orc.kv_quantize_write(wl.key, wl.value, slots, cache, num_q_heads=4, query=qry)
+    K, V, sK, sV = cache_rows(cache)
+    written = np.zeros(K.shape[0], bool)
+    for t in range(T):
+        for h in range(4):
+            qq, ss = orc.quantize(W.bf16_bits_to_f32(qry[t, h]))
+            assert np.array_equal(q8[t, h], qq) and qs[t, h] == ss, "query codes/scale"
+        if slots[t] < 0:
+            continue
+        written[slots[t]] = True
+        for h in range(2):
+            kq, ks = orc.quantize(W.bf16_bits_to_f32(wl.key[t, h]))
+            vq, vs = orc.quantize(W.bf16_bits_to_f32(wl.value[t, h]))
+            assert np.array_equal(K[slots[t], h], kq), f"K layout, token {t} head {h}"
+            assert np.array_equal(V[slots[t], h], vq), f"V layout, token {t} head {h}"
+            assert sK[slots[t], h] == ks and sV[slots[t], h] == vs, "scale layout"
+    assert not K[~written].any() and not V[~written].any(), "write outside its slot"
+    assert not sK[~written].any() and not sV[~written].any(), "scale write outside its slot"
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+def _softmax64(s):
+    s = np.asarray(s, np.float64)
+    e = np.exp(s - s.max())
+    return e / e.sum()
+
+
+def pin_decode_trace(orc, G=32, seed=5):
+    wl = tiny_decode(seed=seed)
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    D, grp = wl.head_dim, wl.num_q_heads // wl.num_kv_heads
+    scale = wl.softmax_scale
+    for b in range(wl.num_seqs):
+        for h in range(wl.num_q_heads):
+            tr = orc.decode_head(q8, qs, cache, wl.block_tables, wl.seq_lens, b, h, w_group=G)
+            L = int(wl.seq_lens[b])
+            sl = seq_slots(wl, b)
+            kv = h // grp
+            acc = K[sl, kv].astype(np.int64) @ q8[b, h].astype(np.int64)
+            assert np.array_equal(tr["acc"].astype(np.int64), acc), f"QK acc (seq {b}, head {h})"
+            assert np.abs(acc).max() <= D * 127 * 127
+            s64 = acc * np.float64(qs[b, h]) * sK[sl, kv].astype(np.float64) * np.float64(scale)
+            assert np.all(np.abs(tr["s"] - s64) <= 2e-7 * np.abs(s64) + 1e-30), "score chain"
+            o_rec = np.zeros_like(tr["o"])
+            for p in range(-(-L // 256)):
+                i0, i1 = 256 * p, min(L, 256 * p + 256)
+                sp = tr["s"][i0:i1].astype(np.float64)
+                assert tr["m"][p] == tr["s"][i0:i1].max(), "partition max"
+                P64 = _softmax64(sp)
+                tol = 1e-6 * (1 + np.abs(sp - sp.max())) * P64 + 1e-45
+                assert np.all(np.abs(tr["P"][i0:i1] - P64) <= tol), "partition softmax"
+                lsum = np.exp(sp - sp.max()).sum()
+                assert abs(tr["l"][p] - lsum) <= 1e-6 * lsum, "partition exp-sum"
+                Wexp = (tr["P"][i0:i1] * sV[sl[i0:i1], kv]).astype(np.float32)
+                assert np.array_equal(tr["W"][i0:i1], Wexp), "W = P * sV"
+                for g0 in range(i0, i1, G):
+                    g1 = min(i1, g0 + G)
+                    check_group_quant(tr["W"][g0:g1], tr["Wq"][g0:g1], tr["sW"][g0 // G],
+                                      f"decode seq {b} head {h} group {g0 // G}")
+                    part = tr["Wq"][g0:g1].astype(np.int64) @ V[sl[g0:g1], kv].astype(np.int64)
+                    assert np.abs(part).max(initial=0) <= G * 127 * 127
+                    o_rec[p] += np.float64(tr["sW"][g0 // G]) * part
+                # error decomposition within the partition (PV article, section 1)
+                Porig = tr["P"][i0:i1].astype(np.float64)
+                tok = np.nonzero(wl.token_seq == b)[0]
+                tok = tok[np.argsort(wl.token_pos[tok])][i0:i1]
+                Vorig = W.bf16_bits_to_f32(wl.value[tok, kv]).astype(np.float64)
+                sVp = sV[sl[i0:i1], kv].astype(np.float64)
+                Vq = V[sl[i0:i1], kv].astype(np.float64)
+                eV = Vorig - sVp[:, None] * Vq
+                sW_tok = np.repeat(tr["sW"][i0 // G:-(-i1 // G)].astype(np.float64), G)
+                sW_tok = sW_tok[:i1 - i0]
+                eW = Porig * sVp - sW_tok * tr["Wq"][i0:i1]
+                lhs = Porig @ Vorig - o_rec[p]
+                rhs = Porig @ eV + eW @ Vq
+                assert np.allclose(lhs, rhs, rtol=0, atol=1e-12 * (1 + np.abs(lhs).max()))
+            assert np.allclose(tr["o"], o_rec, rtol=1e-12, atol=1e-15), "partition output"
+            m = tr["m"].astype(np.float64)
+            w = tr["l"].astype(np.float64) * np.exp(m - m.max())
+            O = (w[:, None] * o_rec).sum(0) / w.sum()
+            assert np.all(np.abs(tr["out"] - O) <= 1e-6 * (np.abs(O) + 1e-3)), "LSE merge"
+
+
+def pin_decode_bruteforce(orc, G=32, seed=6):
+    """Against unquantized fp64 attention, within the bound built from the
+    rounding bounds |eV| <= sV/2 and |eW| <= sW/2 plus the QK term."""
+    wl = tiny_decode(seed=seed, seq_lens=(1, 7, 16, 33, 100, 256, 300, 520))
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    ref = decode_reference_fp64(wl)
+    grp = wl.num_q_heads // wl.num_kv_heads
+    worst = 0.0
+    for b in range(wl.num_seqs):
+        L = int(wl.seq_lens[b])
+        big = 256 * -(-L // 256)   # one partition covering everything
+        for h in range(wl.num_q_heads):
+            kv = h // grp
+            tr = orc.decode_head(q8, qs, cache, wl.block_tables, wl.seq_lens, b, h,
+                                 w_group=G, partition=big)
+            sl = seq_slots(wl, b)
+            tok = np.nonzero(wl.token_seq == b)[0]
+            tok = tok[np.argsort(wl.token_pos[tok])]
+            Vorig = W.bf16_bits_to_f32(wl.value[tok, kv]).astype(np.float64)
+            Korig = W.bf16_bits_to_f32(wl.key[tok, kv]).astype(np.float64)
+            qorig = W.bf16_bits_to_f32(wl.query[wl.decode_query_rows()[b], h]).astype(np.float64)
+            Pe = _softmax64(Korig @ qorig / np.sqrt(wl.head_dim))
+            P = tr["P"].astype(np.float64)
+            sVt = sV[sl, kv].astype(np.float64)
+            sWt = np.repeat(tr["sW"].astype(np.float64), G)[:L]
+            Vq = np.abs(V[sl, kv].astype(np.float64))
+            bound = (np.abs(Pe - P) @ np.abs(Vorig) + (P * sVt / 2).sum()
+                     + (sWt / 2 * (1 + 1e-6)) @ Vq + 1e-6)
+            err = np.abs(tr["out"] - ref[b, h])
+            assert np.all(err <= bound), f"decode seq {b} head {h}: error above bound"
+            worst = max(worst, float((err / bound).max()))
+            out_part = orc.decode_head(q8, qs, cache, wl.block_tables, wl.seq_lens, b, h,
+                                       w_group=G)["out"]
+            assert np.abs(out_part - ref[b, h]).max() < 0.05, "gross error vs fp64 attention"
+    return worst
+
+
+def pin_decode_partition_invariance(orc, G=32, seed=8):
+    wl = tiny_decode(seed=seed, seq_lens=(300, 700, 1000, 257, 513))
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    ex = ORC_EXACT | ORC_NO_WQUANT
+    o256 = orc.paged_decode(q8, qs, cache, wl.block_tables, wl.seq_lens,
+                            num_q_heads=wl.num_q_heads, w_group=G, flags=ex)
+    obig = orc.paged_decode(q8, qs, cache, wl.block_tables, wl.seq_lens,
+                            num_q_heads=wl.num_q_heads, w_group=G, partition=1024, flags=ex)
+    # exact softmax attention over the dequantized cache, written directly
+    grp = wl.num_q_heads // wl.num_kv_heads
+    ref = np.zeros_like(o256, dtype=np.float64)
+    for b in range(wl.num_seqs):
+        sl = seq_slots(wl, b)
+        for h in range(wl.num_q_heads):
+            kv = h // grp
+            acc = K[sl, kv].astype(np.int64) @ q8[b, h].astype(np.int64)
+            s = acc * np.float64(qs[b, h]) * sK[sl, kv].astype(np.float64) * wl.softmax_scale
+            p = _softmax64(s)
+            ref[b, h] = (p * sV[sl, kv].astype(np.float64)) @ V[sl, kv].astype(np.float64)
+    tol = 1e-6 * (np.abs(ref) + 1e-3)
+    assert np.all(np.abs(o256 - ref) <= tol), "partitioned exact decode != single softmax"
+    assert np.all(np.abs(obig - ref) <= tol), "single-partition exact decode != softmax"
+    # quantized: partition size changes only fp32 rounding (Wq tie flips)
+    q256 = orc.paged_decode(q8, qs, cache, wl.block_tables, wl.seq_lens,
+                            num_q_heads=wl.num_q_heads, w_group=G)
+    qbig = orc.paged_decode(q8, qs, cache, wl.block_tables, wl.seq_lens,
+                            num_q_heads=wl.num_q_heads, w_group=G, partition=1024)
+    assert np.abs(q256 - qbig).max() <= 2e-4, "partition size changed the quantized result"
+    assert np.abs(q256 - ref).max() <= 2e-2
+
+
+def pin_decode_special_cases(orc, G=32):
+    # (1) one token: output is the dequantized V of that token
+    wl = tiny_decode(seed=12, seq_lens=(1, 1, 1))
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    out = orc.paged_decode(q8, qs, cache, wl.block_tables, wl.seq_lens,
+                           num_q_heads=wl.num_q_heads, w_group=G)
+    grp = wl.num_q_heads // wl.num_kv_heads
+    for b in range(wl.num_seqs):
+        sl = seq_slots(wl, b)
+        for h in range(wl.num_q_heads):
+            deq = np.float64(sV[sl[0], h // grp]) * V[sl[0], h // grp].astype(np.float64)
+            assert np.all(np.abs(out[b, h] - deq) <= 4e-7 * np.abs(deq) + 1e-30), "L=1"
+    # (2) equal scores (K = 0) and equal V scales: every Wq is 127, output is
+    #     the mean of the dequantized V rows
+    wl = tiny_decode(seed=13, seq_lens=(40, 600))
+    wl.key[:] = 0
+    rng = np.random.default_rng(13)
+    base = np.clip(rng.standard_normal(wl.head_dim), -2.5, 2.5).astype(np.float32)
+    base[0] = 3.0
+    signs = rng.choice([-1.0, 1.0], size=wl.value.shape).astype(np.float32)
+    wl.value[:] = W.f32_to_bf16_bits(signs * base[None, None, :])
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    out = orc.paged_decode(q8, qs, cache, wl.block_tables, wl.seq_lens,
+                           num_q_heads=wl.num_q_heads, w_group=G)
+    for b in range(wl.num_seqs):
+        sl = seq_slots(wl, b)
+        for h in range(wl.num_q_heads):
+            kv = h // grp
+            mean = (sV[sl, kv].astype(np.float64)[:, None] * V[sl, kv]).mean(0)
+            assert np.all(np.abs(out[b, h] - mean) <= 1e-6 * (np.abs(mean) + 1e-2)), "equal scores"
+    # (3) one dominant score: output is that token's dequantized V
+    wl = tiny_decode(seed=14, seq_lens=(90,))
+    qv = W.bf16_bits_to_f32(wl.query[0]).astype(np.float32)
+    j = 37
+    for h in range(wl.num_kv_heads):
+        wl.key[j, h] = W.f32_to_bf16_bits(8.0 * qv[h * grp])
+        wl.query[0, h * grp + 1:(h + 1) * grp] = wl.query[0, h * grp]
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    out = orc.paged_decode(q8, qs, cache, wl.block_tables, wl.seq_lens,
+                           num_q_heads=wl.num_q_heads, w_group=G)
+    sl = seq_slots(wl, 0)
+    for h in range(wl.num_q_heads):
+        kv = h // grp
+        deq = np.float64(sV[sl[j], kv]) * V[sl[j], kv].astype(np.float64)
+        assert np.abs(out[0, h] - deq).max() <= 1e-5 * np.abs(deq).max(), "dominant score"
+    # (4) empty sequence writes zeros
+    wl = tiny_decode(seed=15, seq_lens=(5, 3))
+    cache, q8, qs = orc.fill(wl)
+    out = orc.paged_decode(q8, qs, cache, wl.block_tables, np.array([0, 3], np.int32),
+                           num_q_heads=wl.num_q_heads, w_group=G)
+    assert not out[0].any()
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+def _prefill_rows(wl):
+    qsl = wl.query_start_loc
+    res = []
+    for b in range(wl.num_seqs):
+        chunk = int(qsl[b + 1] - qsl[b])
+        ctx = int(wl.seq_lens[b]) - chunk
+        for j in range(chunk):
+            res.append((int(qsl[b]) + j, b, ctx + j))
+    return res
+
+
+def pin_prefill_exact(orc, G=32, seed=9):
+    """Exact online softmax over history + causal chunk equals plain softmax
+    over the visible keys, for any tile size."""
+    wl = tiny_prefill(seed=seed)
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    grp = wl.num_q_heads // wl.num_kv_heads
+    ex = ORC_EXACT | ORC_NO_WQUANT
+    args = (q8, qs, wl.query_start_loc, wl.seq_lens, cache, wl.block_tables)
+    outs = [orc.prefix_prefill(*args, w_group=G, tile=t, flags=ex) for t in (256, 64, G)]
+    ref = np.zeros_like(outs[0], dtype=np.float64)
+    for r, b, pos in _prefill_rows(wl):
+        sl = seq_slots(wl, b)[:pos + 1]
+        for h in range(wl.num_q_heads):
+            kv = h // grp
+            acc = K[sl, kv].astype(np.int64) @ q8[r, h].astype(np.int64)
+            s = acc * np.float64(qs[r, h]) * sK[sl, kv].astype(np.float64) * wl.softmax_scale
+            p = _softmax64(s)
+            ref[r, h] = (p * sV[sl, kv].astype(np.float64)) @ V[sl, kv].astype(np.float64)
+    for o in outs:
+        assert np.all(np.abs(o - ref) <= 1e-6 * (np.abs(ref) + 1e-3)), "exact prefill != softmax"
+
+
+def pin_prefill_trace(orc, G=32, seed=10, tile=64):
+    wl = tiny_prefill(seed=seed)
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    grp = wl.num_q_heads // wl.num_kv_heads
+    rows = _prefill_rows(wl)
+    ref = prefill_reference_fp64(wl)
+    args = (q8, qs, wl.query_start_loc, wl.seq_lens, cache, wl.block_tables)
+    for r, b, pos in rows[::3]:
+        for h in range(0, wl.num_q_heads, 3):
+            kv = h // grp
+            tr = orc.prefill_row(*args, r, h, w_group=G, tile=tile)
+            assert tr["nk"] == pos + 1
+            sl = seq_slots(wl, b)[:pos + 1]
+            acc = K[sl, kv].astype(np.int64) @ q8[r, h].astype(np.int64)
+            s64 = acc * np.float64(qs[r, h]) * sK[sl, kv].astype(np.float64) * wl.softmax_scale
+            assert np.all(np.abs(tr["s"] - s64) <= 2e-7 * np.abs(s64) + 1e-30), "score chain"
+            nk = pos + 1
+            mrun = -np.inf
+            m_of = np.zeros(nk)
+            for ti, t0 in enumerate(range(0, nk, tile)):
+                t1 = min(nk, t0 + tile)
+                mrun = max(mrun, float(tr["s"][t0:t1].max()))
+                assert tr["m_tile"][ti] == np.float32(mrun), "running max"
+                m_of[t0:t1] = mrun
+            d = tr["s"].astype(np.float64) - m_of
+            pt64 = np.exp(d)
+            assert np.all(np.abs(tr["ptil"] - pt64) <= 1e-6 * (1 + np.abs(d)) * pt64 + 1e-45), "p~"
+            Wt = (tr["ptil"] * sV[sl, kv]).astype(np.float32)
+            for g0 in range(0, nk, G):
+                g1 = min(nk, g0 + G)
+                check_group_quant(Wt[g0:g1], tr["Wq"][g0:g1], tr["sW"][g0 // G],
+                                  f"prefill row {r} head {h} group {g0 // G}")
+            mf = m_of[-1]
+            c_tok = np.exp(m_of - mf)
+            sW_tok = np.repeat(tr["sW"].astype(np.float64), G)[:nk]
+            o = (c_tok * sW_tok * tr["Wq"]) @ V[sl, kv].astype(np.float64)
+            l = (c_tok * tr["ptil"]).sum()
+            assert abs(tr["l"][0] - l) <= 1e-5 * l, "l = sum of unquantized p~"
+            O = o / l
+            assert np.all(np.abs(tr["out"] - O) <= 1e-5 * (np.abs(O) + 1e-3)), "o/l re-assembly"
+            # a-priori bound against unquantized fp64 causal attention
+            tok = np.nonzero(wl.token_seq == b)[0]
+            tok = tok[np.argsort(wl.token_pos[tok])][:nk]
+            Vorig = W.bf16_bits_to_f32(wl.value[tok, kv]).astype(np.float64)
+            Korig = W.bf16_bits_to_f32(wl.key[tok, kv]).astype(np.float64)
+            qorig = W.bf16_bits_to_f32(wl.query[r, h]).astype(np.float64)
+            Pe = _softmax64(Korig @ qorig / np.sqrt(wl.head_dim))
+            P = c_tok * tr["ptil"] / l
+            bound = (np.abs(Pe - P) @ np.abs(Vorig)
+                     + (P * sV[sl, kv] / 2).sum()
+                     + (c_tok * sW_tok / l / 2 * (1 + 1e-6)) @ np.abs(V[sl, kv].astype(np.float64))
+                     + 1e-5)
+            assert np.all(np.abs(tr["out"] - ref[r, h]) <= bound), "prefill error above bound"
+
+
+def pin_prefill_vs_decode(orc, G=32, seed=9):
+    """A prefill row equals a decode of the same query over its visible keys
+    (exactly in real arithmetic; here up to fp32 rounding)."""
+    wl = tiny_prefill(seed=seed)
+    cache, q8, qs = orc.fill(wl)
+    out = orc.prefix_prefill(q8, qs, wl.query_start_loc, wl.seq_lens, cache,
+                             wl.block_tables, w_group=G)
+    worst = 0.0
+    for r, b, pos in _prefill_rows(wl):
+        d = orc.paged_decode(q8[r][None], qs[r][None], cache, wl.block_tables[b][None],
+                             np.array([pos + 1], np.int32), num_q_heads=wl.num_q_heads,
+                             w_group=G)
+        worst = max(worst, float(np.abs(d[0] - out[r]).max()))
+    assert worst <= 2e-4, f"prefill row differs from decode by {worst}"
+    return worst
+
+
+ALL_PINS = [pin_quantize_golden, pin_quantize_bruteforce, pin_cache_layout,
+            pin_decode_trace, pin_decode_bruteforce, pin_decode_partition_invariance,
+            pin_decode_special_cases, pin_prefill_exact, pin_prefill_trace,
+            pin_prefill_vs_decode]

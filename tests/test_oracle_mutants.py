@@ -1,0 +1,114 @@
+"""Mutation tests for the oracle's pins (CPU only).
+
+Each case plants one plausible mistake in a copy of oracle/oracle.cpp (a text
+patch; the shipped oracle has no planted code paths), builds the copy with the
+same flags, and requires at least one pin of tests/pins.py to fail.  This is
+what shows that the pins would catch a dropped term, a wrong sign or index, a
+transposed operand, a wrong rounding rule or a mis-grouped scale -- the last
+one is the negative control the PV-MMAC page describes in section 4 (scales
+computed on tokens other than the ones a matrix instruction consumes).
+"""
+from __future__ import annotations
+
+import sys
+from pathlib import Path
+
+import pytest
+
+import pins
+
+ROOT = Path(__file__).resolve().parent.parent
+SRC = ROOT / "oracle" / "oracle.cpp"
+
+# name -> list of (original text, replacement); every original must occur.
+MUTANTS = {
+    "round_half_even": [("float r = std::round(x[i] / s);",
+                         "float r = std::nearbyint(x[i] / s);")],
+    "round_truncate": [("float r = std::round(x[i] / s);",
+                        "float r = std::trunc(x[i] / s);")],
+    "scale_over_128": [("const float s = amax / 127.0f;", "const float s = amax / 128.0f;")],
+    "gqa_modulo": [("head / (Hq / Hkv)}", "head % Hkv}")],
+    "k_layout_token_major": [
+        ("((((size_t)blk * Hkv + h) * (D / 16) + d / 16) * bs + off) * 16 + d % 16",
+         "((((size_t)blk * Hkv + h) * bs + off) * (D / 16) + d / 16) * 16 + d % 16")],
+    "v_layout_dim_inner": [("(((size_t)blk * Hkv + h) * D + d) * bs + off",
+                            "(((size_t)blk * Hkv + h) * bs + off) * D + d")],
+    "scale_layout_head_major": [("((size_t)blk * bs + off) * Hkv + h",
+                                 "((size_t)blk * Hkv + h) * bs + off")],
+    "page_offset_shift": [("int off(int i) const { return i % c->bs; }",
+                           "int off(int i) const { return (i + 1) % c->bs; }")],
+    "k_unsigned": [("acc += (int64_t)q[d] * (int64_t)sv.kq(i, d);",
+                    "acc += (int64_t)q[d] * (int64_t)(uint8_t)sv.kq(i, d);")],
+    "score_drops_sk": [("  s = s * sk;\n", "  s = s * 1.0f;\n  (void)sk;\n")],
+    "v_scale_reads_k_scale": [("float sv(int i) const { return c->vs[",
+                               "float sv(int i) const { return c->ks[")],
+    "decode_w_without_vscale": [("W[i] = P[i] * sv.sv(i0 + i);", "W[i] = P[i];")],
+    "prefill_w_without_vscale": [("W[j] = pt[j] * sv.sv(t0 + j);", "W[j] = pt[j];")],
+    "decode_p_unnormalized": [("P[i] = e[i] / l;", "P[i] = e[i];")],
+    "exp_base_two": [("return (float)std::exp((double)x);", "return (float)std::exp2((double)x);")],
+    "merge_without_exp": [("const double w = l_part[p] * std::exp(m_part[p] - M);",
+                           "const double w = l_part[p];")],
+    "merge_without_l": [("const double w = l_part[p] * std::exp(m_part[p] - M);",
+                         "const double w = std::exp(m_part[p] - M);")],
+    "misgrouped_w_scale": [(
+        "orc_quantize_w(W, n, wq.data(), &sw);",
+        "orc_quantize_w(W, (n + 1) / 2, wq.data(), &sw);\n"
+        "  for (int j = 0; j < n; ++j)\n"
+        "    wq[j] = sw > 0 ? (int8_t)std::min(127.0f, std::round(W[j] / sw)) : 0;")],
+    "prefill_no_alpha": [("for (int d = 0; d < D; ++d) o[d] *= (double)alpha;", "")],
+    "prefill_l_of_w": [("psum += (double)pt[j];", "psum += (double)pt[j] * sv.sv(t0 + j);")],
+    "prefill_not_causal": [("const int pos = ctx + (row - query_start_loc[b]);",
+                            "const int pos = seq_lens[b] - 1;")],
+    "prefill_excludes_self": [("const int nk = pos + 1;", "const int nk = pos > 0 ? pos : 1;")],
+}
+
+
+def build_mutant(name: str, tmp_path: Path):
+    sys.path.insert(0, str(ROOT))
+    from oracle import Oracle, build as obuild
+    src = SRC.read_text()
+    for old, new in MUTANTS[name]:
+        assert src.count(old) >= 1, f"mutation {name}: pattern not found"
+        src = src.replace(old, new)
+    d = tmp_path / name
+    d.mkdir()
+    (d / "oracle.cpp").write_text(src)
+    lib = obuild.build(d / "oracle.cpp", d / "liboracle.so", extra=["-w"])
+    return Oracle(lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    orc = build_mutant(name, tmp_path)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError as e:
+            failed.append((pin.__name__, str(e).splitlines()[0] if str(e) else ""))
+        except (ValueError, FloatingPointError, IndexError) as e:
+            failed.append((pin.__name__, repr(e)))
+    assert failed, f"no pin caught the planted mistake {name!r}"
+    print(f"{name}: caught by {[f[0] for f in failed]}")
+
+
+def test_misgrouped_scale_blows_past_bound(tmp_path):
+    """Negative control (PV-MMAC page, section 4): scales taken from tokens other
+    than the ones the group consumes push the decode error far past the
+    a-priori bound that the correct grouping satisfies."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    from refmath import decode_reference_fp64
+    good = O.default()
+    bad = build_mutant("misgrouped_w_scale", tmp_path)
+    wl = pins.tiny_decode(seed=31, seq_lens=(200, 256))
+    ref = decode_reference_fp64(wl)
+    errs = []
+    for orc in (good, bad):
+        cache, q8, qs = orc.fill(wl)
+        out = orc.paged_decode(q8, qs, cache, wl.block_tables, wl.seq_lens,
+                               num_q_heads=wl.num_q_heads)
+        errs.append(float(np.abs(out - ref).max()))
+    print(f"max-abs vs fp64: grouped {errs[0]:.3g}, mis-grouped {errs[1]:.3g}")
+    assert errs[1] > 10 * errs[0]
