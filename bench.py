@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the int8-KV paged-attention hot path on one MI355X.
+
+A step is one pass of the hot path over one batch: the fused producer
+quantizes and writes the new token's K/V (and its query) into the paged int8
+cache, then paged decode attends over the whole history.  The default
+workload is decode at 16384 tokens of history (batch 1, 24 q / 4 KV heads,
+head_dim 256, page 16, 1% of V channels x20, W group 32), with inputs
+resident in HBM and rotated over enough distinct cache copies (>= 512 MB) to
+defeat the 256 MB last-level cache.  The chunked-prefill path (2048 queries
+over 16384 cached tokens) is timed as well and reported as int8 TOPS.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+METRIC = ("decode µs & effective KV GB/s (% HBM peak) at 16K; "
+          "prefill-chunk int8 TOPS")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode_L16384",
+                   choices=["decode_L512", "decode_L4096", "decode_L8192", "decode_L16384",
+                            "decode_L32768", "decode_batch16", "mha_producer_decode"])
+    p.add_argument("--w-group", type=int, default=32, choices=[32, 64])
+    p.add_argument("--min-rotation-mb", type=float, default=512.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--prefill-reps", type=int, default=10)
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def build_workload(name, G):
+    import workloads as W
+    b = W.CONFIG_BUILDERS[name]
+    return b(G)
+
+
+def cache_bytes(d):
+    nb, H, D = d.num_blocks, d.num_kv_heads, d.head_dim
+    return nb * H * D * 16 * 2 + nb * 16 * H * 4 * 2
+
+
+def time_decode(args, log_prefix=""):
+    import numpy as np
+    import torch
+
+    import int8_kv_quantized_amd as K
+    wl = build_workload(args.workload, args.w_group)
+    d = K.CacheDesc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    is_q = np.zeros(wl.num_tokens, bool)
+    is_q[wl.query_token_index] = True
+    hist = np.nonzero(~is_q)[0]
+    qi = wl.query_token_index
+
+    copies = max(1, math.ceil(args.min_rotation_mb * 1e6 / cache_bytes(d)))
+    log(f"{log_prefix}workload {wl.name}: S={wl.num_seqs} L_max={wl.max_seq_len} "
+        f"cache {cache_bytes(d) / 1e6:.1f} MB x {copies} copies")
+    base = K.PagedCache.allocate(d)
+    if hist.size:
+        K.kv_quantize_write(d, dev(wl.key[hist]), dev(wl.value[hist]),
+                            dev(wl.slot_mapping[hist]), base)
+    caches = [base] + [K.PagedCache(base.k_cache.clone(), base.v_cache.clone(),
+                                    base.k_scale.clone(), base.v_scale.clone())
+                       for _ in range(copies - 1)]
+    knew, vnew, snew, qnew = (dev(wl.key[qi]), dev(wl.value[qi]), dev(wl.slot_mapping[qi]),
+                              dev(wl.query))
+    T = int(qi.shape[0])
+    q8 = torch.empty((T, d.num_q_heads, d.head_dim), dtype=torch.int8, device="cuda")
+    qs = torch.empty((T, d.num_q_heads), dtype=torch.float32, device="cuda")
+    per_seq = T // wl.num_seqs
+    if per_seq == 1:
+        dq8, dqs = q8, qs
+    else:
+        dq8 = torch.empty((wl.num_seqs, d.num_q_heads, d.head_dim), dtype=torch.int8,
+                          device="cuda")
+        dqs = torch.empty((wl.num_seqs, d.num_q_heads), dtype=torch.float32, device="cuda")
+    bt, sl = dev(wl.block_tables), dev(wl.seq_lens)
+    ws = torch.zeros(K.paged_decode_workspace_bytes(d, wl.num_seqs, wl.max_seq_len),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.num_seqs, d.num_q_heads, d.head_dim), dtype=torch.float32,
+                      device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c = caches[i % copies]
+        if ev is not None:
+            ev[0].record(stream)
+        K.kv_quantize_write(d, knew, vnew, snew, c, query=qnew, q_int8=q8, q_scale=qs,
+                            stream=stream)
+        if per_seq != 1:
+            dq8.copy_(q8.view(wl.num_seqs, per_seq, *q8.shape[1:])[:, -1])
+            dqs.copy_(qs.view(wl.num_seqs, per_seq, -1)[:, -1])
+        if ev is not None:
+            ev[1].record(stream)
+        K.paged_decode_int8(d, dq8, dqs, c, bt, sl, wl.max_seq_len, w_group=args.w_group,
+                            workspace=ws, out=out, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    prod_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    return dict(wl=wl, desc=d, copies=copies, ms_per_step=ms_total / args.steps,
+                producer_us=1e3 * float(np.mean(prod_ms)), decode_us=1e3 * float(np.mean(dec_ms)),
+                decode_us_p50=1e3 * float(np.median(dec_ms)))
+
+
+def time_prefill(reps, G=32):
+    import numpy as np
+    import torch
+
+    import int8_kv_quantized_amd as K
+    import workloads as W
+    wl = W.cfg4_prefill(w_group=G)
+    d = K.CacheDesc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    cache = K.PagedCache.allocate(d)
+    is_q = np.zeros(wl.num_tokens, bool)
+    is_q[wl.query_token_index] = True
+    hist = np.nonzero(~is_q)[0]
+    qi = wl.query_token_index
+    K.kv_quantize_write(d, dev(wl.key[hist]), dev(wl.value[hist]), dev(wl.slot_mapping[hist]),
+                        cache)
+    q8, qs = K.kv_quantize_write(d, dev(wl.key[qi]), dev(wl.value[qi]),
+                                 dev(wl.slot_mapping[qi]), cache, query=dev(wl.query))
+    qsl, sl, bt = dev(wl.query_start_loc), dev(wl.seq_lens), dev(wl.block_tables)
+    out = torch.empty((q8.shape[0], d.num_q_heads, d.head_dim), dtype=torch.float32,
+                      device="cuda")
+    chunk = int(qi.shape[0])
+    for _ in range(2):
+        K.prefix_prefill_int8(d, q8, qs, qsl, sl, cache, bt, chunk, w_group=G, out=out)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        K.prefix_prefill_int8(d, q8, qs, qsl, sl, cache, bt, chunk, w_group=G, out=out)
+        e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    hist_len = int(wl.seq_lens[0]) - chunk
+    visible = sum(hist_len + j + 1 for j in range(chunk))  # causal pairs per head
+    ops = 2 * 2 * d.head_dim * d.num_q_heads * visible
+    return dict(us=us, ops=ops, tops=ops / (us * 1e-6) / 1e12, workload=wl.name)
+
+
+def cpu_baseline(wl, G, seconds):
+    """The oracle, single-threaded, on the same decode workload (whole calls)."""
+    import numpy as np
+
+    import oracle
+    orc = oracle.default()
+    cache, q8, qs = orc.fill(wl)
+    rows = wl.decode_query_rows()
+    q8, qs = q8[rows], qs[rows]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.paged_decode(q8, qs, cache, wl.block_tables, wl.seq_lens,
+                         num_q_heads=wl.num_q_heads, w_group=G)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = wl.effective_kv_bytes() * reps / el / 1e9
+    return dict(value=round(gbs, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"{reps} whole decode calls of {wl.name} ({el:.1f} s, single thread; "
+                       f"host has {os.cpu_count()} logical CPUs)")
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU component).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import int8_kv_quantized_amd as K
+    K.load_library()
+
+    r = time_decode(args)
+    wl = r["wl"]
+    eff = wl.effective_kv_bytes()
+    step_s = r["ms_per_step"] * 1e-3
+    value = eff / step_s / 1e9
+    achieved = eff / (r["decode_us"] * 1e-6) / 1e9
+    log(f"decode: {r['decode_us']:.2f} us/launch (p50 {r['decode_us_p50']:.2f}), producer "
+        f"{r['producer_us']:.2f} us, step {r['ms_per_step'] * 1e3:.2f} us, "
+        f"{achieved:.0f} GB/s effective ({100 * achieved / HBM_PEAK_GBS:.1f}% of peak)")
+    extra = dict(decode_us=round(r["decode_us"], 3), decode_us_p50=round(r["decode_us_p50"], 3),
+                 producer_us=round(r["producer_us"], 3), effective_kv_bytes=eff,
+                 cache_copies_rotated=r["copies"])
+    if not args.no_prefill:
+        pf = time_prefill(args.prefill_reps)
+        log(f"prefill {pf['workload']}: {pf['us']:.1f} us, {pf['tops']:.1f} int8 TOPS "
+            f"({100 * pf['tops'] / INT8_PEAK_TOPS:.1f}% of peak)")
+        extra.update(prefill_us=round(pf["us"], 2), prefill_int8_tops=round(pf["tops"], 2),
+                     prefill_frac_of_int8_peak=round(pf["tops"] / INT8_PEAK_TOPS, 4),
+                     prefill_ops=pf["ops"])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.w_group, args.cpu_seconds)
+        log(f"cpu baseline: {cpu}")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.num_seqs, "seq_len": wl.max_seq_len,
+                   "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "page_size": 16, "w_group": args.w_group,
+                   "partition": 256,
+                   "step": "kv_quantize_write(new token, with Q) + paged_decode_int8"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

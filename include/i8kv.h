@@ -1,0 +1,178 @@
+/*
+ * i8kv -- paged attention over an INT8 KV cache, native to AMD MI355X (gfx950).
+ *
+ * C ABI of the library libi8kv.so.  Three operations, as defined on the pages
+ *   [KV] "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
+ *        DCU" (part 1 of the series), and
+ *   [PV] "Implementing INT8 PV MMAC on a gfx936 DCU: V-scale fusion,
+ *        probability quantization, fragment grouping" (part 3):
+ *
+ *   i8kv_kv_quantize_write  -- the fused KV producer ([KV] sections 2.1-2.3)
+ *   i8kv_paged_decode_int8  -- decode over 256-token partitions ([KV] 3.3,
+ *                              [PV] 2.2, merge by log-sum-exp weights)
+ *   i8kv_prefix_prefill_int8 -- chunked prefill with history in one online
+ *                              softmax ([KV] 3.2, [PV] 2.1)
+ *
+ * Conventions for every call
+ *  - Tensor arguments are DEVICE pointers owned by the caller, C-contiguous in
+ *    the layouts given below.  The library never allocates, frees or
+ *    synchronizes, keeps no global state and is re-entrant; all work is
+ *    enqueued on `stream` (NULL = the default stream) and is asynchronous.
+ *  - bf16 tensors are passed as their 16-bit patterns (uint16_t).
+ *  - Cache layouts ([KV] 2.3), with x = 16 head-dim bytes per token:
+ *      k_cache [num_blocks, Hkv, D/16, block_size, 16]  int8
+ *      v_cache [num_blocks, Hkv, D, block_size]         int8
+ *      k_scale, v_scale [num_blocks, block_size, Hkv]   fp32
+ *    Token position i of a sequence lives in page block_tables[s][i / 16] at
+ *    offset i % 16.  Q head h reads KV head h / (Hq / Hkv).
+ *  - Quantization ([KV] 2.1): amax = max|x|, scale = amax / 127 (fp32, IEEE
+ *    division), q = clamp(round(x / scale), -127, 127), rounding half away
+ *    from zero; amax = 0 stores scale 0 and all-zero codes.
+ *  - Status: argument and shape checks run on the host BEFORE anything is
+ *    enqueued; on any non-OK status nothing has been launched, except
+ *    I8KV_ERR_LAUNCH, which reports a failed enqueue.  No C++ exception
+ *    crosses the ABI.
+ *  - Supported shapes: block_size = 16; head_dim in {64, 128, 256};
+ *    Hq % Hkv = 0 with Hq / Hkv <= 16; w_group in {32, 64};
+ *    partition_size = 256.  Other values return I8KV_ERR_UNSUPPORTED.
+ *  - Preconditions not checked on the host (they live in device memory):
+ *    block ids < num_blocks, slots < num_blocks * block_size, finite inputs,
+ *    seq_lens[s] <= max_seq_len and <= 16 * max_blocks_per_seq.
+ */
+#ifndef I8KV_H
+#define I8KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define I8KV_ABI_VERSION 1
+
+typedef enum {
+  I8KV_OK = 0,
+  I8KV_ERR_NULL = 1,          /* a required pointer is NULL */
+  I8KV_ERR_INVALID_ARG = 2,   /* negative count, inconsistent sizes */
+  I8KV_ERR_UNSUPPORTED = 3,   /* shape outside the supported set above */
+  I8KV_ERR_WORKSPACE = 4,     /* workspace missing or too small */
+  I8KV_ERR_LAUNCH = 5         /* the HIP runtime refused the launch */
+} i8kv_status;
+
+/* Geometry shared by the cache and the attention calls. */
+typedef struct {
+  int32_t num_q_heads;   /* Hq */
+  int32_t num_kv_heads;  /* Hkv */
+  int32_t head_dim;      /* D */
+  int32_t block_size;    /* tokens per page; must be 16 */
+  int32_t num_blocks;    /* pages in the cache */
+} i8kv_cache_desc;
+
+/* hipStream_t, passed as an opaque handle. */
+typedef void* i8kv_stream_t;
+
+/*
+ * Fused KV producer ([KV] 2.2): for each token t < num_tokens, quantize K and
+ * V per (token, KV head) and write codes and scales to slot slot_mapping[t]
+ * (page slot / 16, offset slot % 16); a negative slot skips the cache write.
+ * When `query` is non-NULL, also quantize Q once per (token, q head) into
+ * q_int8 / q_scale, for reuse by every partition that reads it.
+ *   key, value   [T, Hkv, D] bf16          query  [T, Hq, D] bf16 or NULL
+ *   q_int8       [T, Hq, D] int8           q_scale [T, Hq] fp32
+ *   slot_mapping [T] int32
+ * Errors: NULL for missing key/value/slot_mapping/cache pointers or for
+ * q_int8/q_scale missing while query is given; INVALID_ARG for num_tokens < 0.
+ * num_tokens = 0 enqueues nothing.
+ */
+i8kv_status i8kv_kv_quantize_write(const i8kv_cache_desc* desc, int32_t num_tokens,
+                                   const uint16_t* key, const uint16_t* value,
+                                   const uint16_t* query, int8_t* q_int8,
+                                   float* q_scale, const int32_t* slot_mapping,
+                                   int8_t* k_cache, int8_t* v_cache,
+                                   float* k_scale, float* v_scale,
+                                   i8kv_stream_t stream);
+
+/*
+ * Bytes of device workspace that i8kv_paged_decode_int8 needs for num_seqs
+ * sequences of at most max_seq_len tokens: per-partition (m, l, output)
+ * partials plus merge counters.  Returns 0 for invalid arguments.
+ */
+size_t i8kv_paged_decode_workspace_bytes(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                         int32_t max_seq_len, int32_t partition_size);
+
+/*
+ * Paged decode over the INT8 cache ([KV] 3.3; [PV] 2.2), one query per
+ * sequence attending to its seq_lens[s] cached tokens:
+ *   score_i = ((acc_i * sQ) * sK_i) * softmax_scale, acc_i the int32 dot
+ *             product of the int8 query and key;
+ *   per 256-token partition p: m_p = max score, e_i = exp(score_i - m_p),
+ *             l_p = sum e_i, P_i = e_i / l_p, W_i = P_i * sV_i;
+ *   per aligned group of w_group tokens: sW = max W / 127, Wq = round(W / sW),
+ *             o_p += sW * (Wq x Vq) with an int8 x int8 -> int32 product;
+ *   merge:    O = sum_p w_p o_p / sum_p w_p, w_p = l_p exp(m_p - max m).
+ *   q_int8 [S, Hq, D], q_scale [S, Hq]   (as written by the producer)
+ *   block_tables [S, max_blocks_per_seq] int32, seq_lens [S] int32
+ *   out [S, Hq, D] fp32, fully overwritten (seq_len 0 gives zeros)
+ * workspace: device memory of at least
+ *   i8kv_paged_decode_workspace_bytes(desc, S, max_seq_len, partition_size)
+ *   bytes, zero-filled once by the caller when it is allocated; every call
+ *   leaves its counters at zero again.  Calls that run concurrently must use
+ *   different workspaces.
+ * Errors: NULL, INVALID_ARG (S < 0, max_seq_len < 0, max_seq_len larger than
+ * 16 * max_blocks_per_seq), UNSUPPORTED, WORKSPACE.
+ */
+i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                   const int8_t* q_int8, const float* q_scale,
+                                   const int8_t* k_cache, const int8_t* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* seq_lens, int32_t max_seq_len,
+                                   int32_t partition_size, int32_t w_group,
+                                   float softmax_scale, void* workspace,
+                                   size_t workspace_bytes, float* out,
+                                   i8kv_stream_t stream);
+
+/* Workspace bytes for i8kv_prefix_prefill_int8 (currently none needed). */
+size_t i8kv_prefix_prefill_workspace_bytes(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                           int32_t total_q);
+
+/*
+ * Chunked prefill with history ([KV] 3.2; [PV] 2.1).  Sequence s owns query
+ * rows query_start_loc[s] .. query_start_loc[s+1]-1 (its chunk of
+ * c_s tokens); the chunk's own K/V must already be in the cache (written by
+ * the producer), so seq_lens[s] counts history + chunk.  Row j of the chunk
+ * sits at absolute position seq_lens[s] - c_s + j and sees keys 0..position
+ * (causal within the chunk).  History and chunk go through ONE online softmax:
+ *   m' = max(m, max s), alpha = exp(m - m'), p~_i = exp(s_i - m'),
+ *   W_i = p~_i * sV_i, group-quantized per aligned w_group keys as in decode,
+ *   o = alpha o + sum_g sW (Wq x Vq), l = alpha l + sum p~_i, O = o / l.
+ *   q_int8 [total_q, Hq, D], q_scale [total_q, Hq]
+ *   query_start_loc [S+1] int32, seq_lens [S] int32,
+ *   block_tables [S, max_blocks_per_seq] int32
+ *   max_query_len >= every chunk length (sizes the launch grid)
+ *   out [total_q, Hq, D] fp32, fully overwritten.
+ * Errors: NULL, INVALID_ARG, UNSUPPORTED (as for decode), WORKSPACE.
+ */
+i8kv_status i8kv_prefix_prefill_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                     int32_t total_q, int32_t max_query_len,
+                                     const int8_t* q_int8, const float* q_scale,
+                                     const int32_t* query_start_loc,
+                                     const int32_t* seq_lens, const int8_t* k_cache,
+                                     const int8_t* v_cache, const float* k_scale,
+                                     const float* v_scale, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, int32_t w_group,
+                                     float softmax_scale, void* workspace,
+                                     size_t workspace_bytes, float* out,
+                                     i8kv_stream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* i8kv_status_string(i8kv_status status);
+
+/* I8KV_ABI_VERSION of the loaded library. */
+int32_t i8kv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* I8KV_H */

@@ -1,0 +1,28 @@
+"""Paged attention over an INT8 KV cache on AMD MI355X (gfx950).
+
+Python binding of libi8kv.so.  Every step of the computation runs in the HIP
+kernels behind the C ABI (include/i8kv.h); this package only marshals
+arguments (torch tensors or raw device pointers) and checks shapes on the
+host.  Importing it does not load the library; the first call does, and it
+fails loudly if the library has not been built -- there is no fallback.
+
+    kv_quantize_write(desc, key, value, slot_mapping, cache, query=None, ...)
+    paged_decode_workspace_bytes(desc, num_seqs, max_seq_len)
+    paged_decode_int8(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
+    prefix_prefill_int8(desc, q_int8, q_scale, query_start_loc, seq_lens,
+                        cache, block_tables, ...)
+"""
+from ._binding import (  # noqa: F401
+    CacheDesc,
+    I8KVError,
+    PagedCache,
+    abi_version,
+    kv_quantize_write,
+    lib_path,
+    load_library,
+    paged_decode_int8,
+    paged_decode_workspace_bytes,
+    prefix_prefill_int8,
+    prefix_prefill_workspace_bytes,
+    status_string,
+)

@@ -1,0 +1,294 @@
+"""ctypes binding of libi8kv.so: argument marshalling and host-side shape checks.
+
+Names follow the C ABI in include/i8kv.h without the ``i8kv_`` prefix.
+Tensor arguments may be torch tensors on the GPU (checked for dtype, shape,
+contiguity and device) or raw device pointers (ints, trusted as given).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+import math
+from pathlib import Path
+from typing import Optional
+
+HERE = Path(__file__).resolve().parent
+I8KV_OK = 0
+_STATUS = {0: "ok", 1: "null pointer argument", 2: "invalid argument",
+           3: "unsupported shape or parameter", 4: "workspace missing or too small",
+           5: "kernel launch failed"}
+
+
+class I8KVError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: status {status} ({_STATUS.get(status, 'unknown')})")
+        self.status = status
+
+
+class CacheDesc(C.Structure):
+    _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("block_size", C.c_int32),
+                ("num_blocks", C.c_int32)]
+
+    def __init__(self, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size=16):
+        super().__init__(num_q_heads, num_kv_heads, head_dim, block_size, num_blocks)
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def __repr__(self):
+        return (f"CacheDesc(Hq={self.num_q_heads}, Hkv={self.num_kv_heads}, "
+                f"D={self.head_dim}, bs={self.block_size}, nb={self.num_blocks})")
+
+
+_lib = None
+
+
+def lib_path() -> Path:
+    return HERE / "libi8kv.so"
+
+
+def load_library():
+    """Load libi8kv.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = lib_path()
+    if not p.exists():
+        raise RuntimeError(f"{p} is missing: build it with int8_kv_quantized_amd.build.build() "
+                           "(there is no fallback path)")
+    lib = C.CDLL(str(p))
+    P, I32, F, SZ = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
+    D = C.POINTER(CacheDesc)
+    lib.i8kv_abi_version.restype = I32
+    lib.i8kv_abi_version.argtypes = []
+    lib.i8kv_status_string.restype = C.c_char_p
+    lib.i8kv_status_string.argtypes = [C.c_int]
+    lib.i8kv_kv_quantize_write.restype = C.c_int
+    lib.i8kv_kv_quantize_write.argtypes = [D, I32] + [P] * 10 + [P]
+    lib.i8kv_paged_decode_workspace_bytes.restype = SZ
+    lib.i8kv_paged_decode_workspace_bytes.argtypes = [D, I32, I32, I32]
+    lib.i8kv_paged_decode_int8.restype = C.c_int
+    lib.i8kv_paged_decode_int8.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F, P, SZ,
+                                                                 P, P])
+    lib.i8kv_prefix_prefill_workspace_bytes.restype = SZ
+    lib.i8kv_prefix_prefill_workspace_bytes.argtypes = [D, I32, I32]
+    lib.i8kv_prefix_prefill_int8.restype = C.c_int
+    lib.i8kv_prefix_prefill_int8.argtypes = ([D, I32, I32, I32] + [P] * 9 + [I32, I32, F, P, SZ,
+                                                                            P, P])
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load_library().i8kv_abi_version())
+
+
+def status_string(status: int) -> str:
+    return load_library().i8kv_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _is_tensor(x) -> bool:
+    return hasattr(x, "data_ptr") and hasattr(x, "dtype")
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return C.c_void_p(x)
+    if _is_tensor(x):
+        return C.c_void_p(x.data_ptr())
+    raise TypeError(f"expected a tensor, a device pointer or None, got {type(x)}")
+
+
+def _check(x, name, dtype, shape=None):
+    """Validate a torch tensor argument (raw pointers are passed through)."""
+    if x is None or isinstance(x, int):
+        return
+    import torch
+    ok = x.dtype in dtype if isinstance(dtype, tuple) else x.dtype == dtype
+    if not ok:
+        raise ValueError(f"{name}: dtype {x.dtype}, expected {dtype}")
+    if not x.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None:
+        want = tuple(int(s) for s in shape)
+        if tuple(x.shape) != want:
+            raise ValueError(f"{name}: shape {tuple(x.shape)}, expected {want}")
+    del torch
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _raise(fn, st):
+    if st != I8KV_OK:
+        raise I8KVError(fn, st)
+
+
+@dataclasses.dataclass
+class PagedCache:
+    """Device tensors of one paged int8 cache (layouts of include/i8kv.h)."""
+    k_cache: object   # int8  [nb, Hkv, D/16, 16, 16]
+    v_cache: object   # int8  [nb, Hkv, D, 16]
+    k_scale: object   # fp32  [nb, 16, Hkv]
+    v_scale: object   # fp32  [nb, 16, Hkv]
+
+    @classmethod
+    def allocate(cls, desc: CacheDesc, device="cuda", zero=True):
+        import torch
+        nb, H, D, bs = desc.num_blocks, desc.num_kv_heads, desc.head_dim, desc.block_size
+        mk = torch.zeros if zero else torch.empty
+        return cls(mk((nb, H, D // 16, bs, 16), dtype=torch.int8, device=device),
+                   mk((nb, H, D, bs), dtype=torch.int8, device=device),
+                   mk((nb, bs, H), dtype=torch.float32, device=device),
+                   mk((nb, bs, H), dtype=torch.float32, device=device))
+
+    def check(self, desc: CacheDesc):
+        import torch
+        nb, H, D, bs = desc.num_blocks, desc.num_kv_heads, desc.head_dim, desc.block_size
+        _check(self.k_cache, "k_cache", torch.int8, (nb, H, D // 16, bs, 16))
+        _check(self.v_cache, "v_cache", torch.int8, (nb, H, D, bs))
+        _check(self.k_scale, "k_scale", torch.float32, (nb, bs, H))
+        _check(self.v_scale, "v_scale", torch.float32, (nb, bs, H))
+
+
+# ---------------------------------------------------------------------------
+# the three operations
+# ---------------------------------------------------------------------------
+def kv_quantize_write(desc: CacheDesc, key, value, slot_mapping, cache: PagedCache,
+                      query=None, q_int8=None, q_scale=None, num_tokens: Optional[int] = None,
+                      stream=None):
+    """Fused producer: quantize K/V (and Q) and write the paged cache.
+
+    Returns ``(q_int8, q_scale)`` (allocated here when ``query`` is given and
+    they are not).
+    """
+    import torch
+    lib = load_library()
+    if num_tokens is None:
+        num_tokens = int(key.shape[0])
+    T, Hq, Hkv, D = num_tokens, desc.num_q_heads, desc.num_kv_heads, desc.head_dim
+    bits16 = (torch.bfloat16, torch.int16, torch.uint16)
+    _check(key, "key", bits16)
+    _check(value, "value", bits16)
+    _check(query, "query", bits16)
+    for name, x in (("key", key), ("value", value)):
+        if _is_tensor(x) and tuple(x.shape) != (T, Hkv, D):
+            raise ValueError(f"{name}: shape {tuple(x.shape)}, expected {(T, Hkv, D)}")
+    _check(slot_mapping, "slot_mapping", torch.int32, (T,))
+    cache.check(desc)
+    if query is not None:
+        if _is_tensor(query) and tuple(query.shape) != (T, Hq, D):
+            raise ValueError(f"query: shape {tuple(query.shape)}, expected {(T, Hq, D)}")
+        if q_int8 is None:
+            q_int8 = torch.empty((T, Hq, D), dtype=torch.int8, device=key.device)
+        if q_scale is None:
+            q_scale = torch.empty((T, Hq), dtype=torch.float32, device=key.device)
+        _check(q_int8, "q_int8", torch.int8, (T, Hq, D))
+        _check(q_scale, "q_scale", torch.float32, (T, Hq))
+    st = lib.i8kv_kv_quantize_write(
+        C.byref(desc), T, _ptr(key), _ptr(value), _ptr(query), _ptr(q_int8), _ptr(q_scale),
+        _ptr(slot_mapping), _ptr(cache.k_cache), _ptr(cache.v_cache), _ptr(cache.k_scale),
+        _ptr(cache.v_scale), _stream(stream))
+    _raise("kv_quantize_write", st)
+    return q_int8, q_scale
+
+
+def paged_decode_workspace_bytes(desc: CacheDesc, num_seqs: int, max_seq_len: int,
+                                 partition_size: int = 256) -> int:
+    return int(load_library().i8kv_paged_decode_workspace_bytes(
+        C.byref(desc), int(num_seqs), int(max_seq_len), int(partition_size)))
+
+
+def paged_decode_int8(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables,
+                      seq_lens, max_seq_len: int, w_group: int = 32,
+                      partition_size: int = 256, softmax_scale: Optional[float] = None,
+                      workspace=None, out=None, stream=None):
+    """Paged decode over the int8 cache; returns ``out`` [S, Hq, D] fp32.
+
+    ``workspace`` must hold paged_decode_workspace_bytes(...) bytes and be
+    zero-filled when first allocated (allocated and zeroed here if None).
+    """
+    import torch
+    lib = load_library()
+    S = int(seq_lens.shape[0]) if _is_tensor(seq_lens) else int(q_int8.shape[0])
+    Hq, D = desc.num_q_heads, desc.head_dim
+    _check(q_int8, "q_int8", torch.int8, (S, Hq, D))
+    _check(q_scale, "q_scale", torch.float32, (S, Hq))
+    cache.check(desc)
+    _check(block_tables, "block_tables", torch.int32)
+    if not _is_tensor(block_tables):
+        raise ValueError("block_tables must be a tensor (its width is needed)")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError(f"block_tables: shape {tuple(block_tables.shape)}, expected ({S}, *)")
+    _check(seq_lens, "seq_lens", torch.int32, (S,))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    need = paged_decode_workspace_bytes(desc, S, max_seq_len, partition_size)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=block_tables.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if _is_tensor(workspace) else need
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=block_tables.device)
+    _check(out, "out", torch.float32, (S, Hq, D))
+    st = lib.i8kv_paged_decode_int8(
+        C.byref(desc), S, _ptr(q_int8), _ptr(q_scale), _ptr(cache.k_cache),
+        _ptr(cache.v_cache), _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(partition_size),
+        int(w_group), float(softmax_scale), _ptr(workspace), int(ws_bytes), _ptr(out),
+        _stream(stream))
+    _raise("paged_decode_int8", st)
+    return out
+
+
+def prefix_prefill_workspace_bytes(desc: CacheDesc, num_seqs: int, total_q: int) -> int:
+    return int(load_library().i8kv_prefix_prefill_workspace_bytes(
+        C.byref(desc), int(num_seqs), int(total_q)))
+
+
+def prefix_prefill_int8(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_lens,
+                        cache: PagedCache, block_tables, max_query_len: int,
+                        w_group: int = 32, softmax_scale: Optional[float] = None,
+                        out=None, workspace=None, stream=None):
+    """Chunked prefill with history; returns ``out`` [total_q, Hq, D] fp32."""
+    import torch
+    lib = load_library()
+    Tq = int(q_int8.shape[0])
+    S = int(seq_lens.shape[0])
+    Hq, D = desc.num_q_heads, desc.head_dim
+    _check(q_int8, "q_int8", torch.int8, (Tq, Hq, D))
+    _check(q_scale, "q_scale", torch.float32, (Tq, Hq))
+    _check(query_start_loc, "query_start_loc", torch.int32, (S + 1,))
+    _check(seq_lens, "seq_lens", torch.int32, (S,))
+    cache.check(desc)
+    _check(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError(f"block_tables: shape {tuple(block_tables.shape)}, expected ({S}, *)")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((Tq, Hq, D), dtype=torch.float32, device=q_int8.device)
+    _check(out, "out", torch.float32, (Tq, Hq, D))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.i8kv_prefix_prefill_int8(
+        C.byref(desc), S, Tq, int(max_query_len), _ptr(q_int8), _ptr(q_scale),
+        _ptr(query_start_loc), _ptr(seq_lens), _ptr(cache.k_cache), _ptr(cache.v_cache),
+        _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]), int(w_group), float(softmax_scale), _ptr(workspace),
+        int(ws_bytes), _ptr(out), _stream(stream))
+    _raise("prefix_prefill_int8", st)
+    return out

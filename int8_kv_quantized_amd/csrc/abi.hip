@@ -1,0 +1,222 @@
+// C ABI of libi8kv: argument validation on the host, then one launch.
+// Every check below runs before anything is enqueued; no exception crosses
+// the ABI.  The declarations and their documentation are in include/i8kv.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/i8kv.h"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace i8kv;
+
+constexpr int32_t kMaxSeqLen = 1 << 20;  // 4096 partitions: 64 x 64 merge tree
+constexpr int32_t kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+i8kv_status check_desc(const i8kv_cache_desc* d) {
+  if (!d) return I8KV_ERR_NULL;
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 || d->num_blocks <= 0 ||
+      d->block_size <= 0)
+    return I8KV_ERR_INVALID_ARG;
+  if (d->block_size != kBlockSize) return I8KV_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return I8KV_ERR_UNSUPPORTED;
+  if (d->num_q_heads % d->num_kv_heads != 0) return I8KV_ERR_UNSUPPORTED;
+  if (d->num_q_heads / d->num_kv_heads > 16) return I8KV_ERR_UNSUPPORTED;
+  if (d->num_kv_heads > kMaxGridYZ) return I8KV_ERR_UNSUPPORTED;
+  return I8KV_OK;
+}
+
+i8kv_status from_hip(hipError_t e) { return e == hipSuccess ? I8KV_OK : I8KV_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t i8kv_abi_version(void) { return I8KV_ABI_VERSION; }
+
+const char* i8kv_status_string(i8kv_status s) {
+  switch (s) {
+    case I8KV_OK: return "ok";
+    case I8KV_ERR_NULL: return "null pointer argument";
+    case I8KV_ERR_INVALID_ARG: return "invalid argument";
+    case I8KV_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+    case I8KV_ERR_WORKSPACE: return "workspace missing or too small";
+    case I8KV_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+i8kv_status i8kv_kv_quantize_write(const i8kv_cache_desc* desc, int32_t num_tokens,
+                                   const uint16_t* key, const uint16_t* value,
+                                   const uint16_t* query, int8_t* q_int8, float* q_scale,
+                                   const int32_t* slot_mapping, int8_t* k_cache,
+                                   int8_t* v_cache, float* k_scale, float* v_scale,
+                                   i8kv_stream_t stream) {
+  i8kv_status st = check_desc(desc);
+  if (st != I8KV_OK) return st;
+  if (!key || !value || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+    return I8KV_ERR_NULL;
+  if (query && (!q_int8 || !q_scale)) return I8KV_ERR_NULL;
+  if (num_tokens < 0) return I8KV_ERR_INVALID_ARG;
+  if (!aligned16(key) || !aligned16(value) || (query && (!aligned16(query) || !aligned16(q_int8))) ||
+      !aligned16(k_cache) || !aligned16(v_cache))
+    return I8KV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return I8KV_OK;
+  ProducerArgs a{};
+  a.num_tokens = num_tokens;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.head_dim = desc->head_dim;
+  a.num_blocks = desc->num_blocks;
+  a.key = key;
+  a.value = value;
+  a.query = query;
+  a.q_int8 = q_int8;
+  a.q_scale = q_scale;
+  a.slot_mapping = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return from_hip(launch_kv_quantize_write(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t i8kv_paged_decode_workspace_bytes(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                         int32_t max_seq_len, int32_t partition_size) {
+  if (check_desc(desc) != I8KV_OK || num_seqs < 0 || max_seq_len < 0 ||
+      max_seq_len > kMaxSeqLen || partition_size != kPartition)
+    return 0;
+  const DecodePlan p = make_decode_plan(num_seqs, desc->num_kv_heads,
+                                        desc->num_q_heads / desc->num_kv_heads,
+                                        desc->head_dim, max_seq_len);
+  return p.bytes;
+}
+
+i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                   const int8_t* q_int8, const float* q_scale,
+                                   const int8_t* k_cache, const int8_t* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* seq_lens, int32_t max_seq_len,
+                                   int32_t partition_size, int32_t w_group,
+                                   float softmax_scale, void* workspace,
+                                   size_t workspace_bytes, float* out,
+                                   i8kv_stream_t stream) {
+  i8kv_status st = check_desc(desc);
+  if (st != I8KV_OK) return st;
+  if (!q_int8 || !q_scale || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables ||
+      !seq_lens || !out)
+    return I8KV_ERR_NULL;
+  if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq <= 0) return I8KV_ERR_INVALID_ARG;
+  if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * kBlockSize) return I8KV_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return I8KV_ERR_INVALID_ARG;
+  if (partition_size != kPartition || (w_group != 32 && w_group != 64))
+    return I8KV_ERR_UNSUPPORTED;
+  if (max_seq_len > kMaxSeqLen || num_seqs > kMaxGridYZ) return I8KV_ERR_UNSUPPORTED;
+  if (!aligned16(q_int8) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return I8KV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return I8KV_OK;
+  const int32_t grp = desc->num_q_heads / desc->num_kv_heads;
+  const DecodePlan p =
+      make_decode_plan(num_seqs, desc->num_kv_heads, grp, desc->head_dim, max_seq_len);
+  if (!workspace || workspace_bytes < p.bytes) return I8KV_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8KV_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  DecodeArgs a{};
+  a.num_seqs = num_seqs;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.group = grp;
+  a.head_dim = desc->head_dim;
+  a.num_blocks = desc->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.w_group = w_group;
+  a.softmax_scale = softmax_scale;
+  a.q_int8 = q_int8;
+  a.q_scale = q_scale;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.part_o = reinterpret_cast<float*>(ws + p.off_part_o);
+  a.part_ml = reinterpret_cast<float*>(ws + p.off_part_ml);
+  a.node_o = reinterpret_cast<float*>(ws + p.off_node_o);
+  a.node_ml = reinterpret_cast<float*>(ws + p.off_node_ml);
+  a.cnt1 = reinterpret_cast<int32_t*>(ws + p.off_cnt1);
+  a.cnt2 = reinterpret_cast<int32_t*>(ws + p.off_cnt2);
+  a.max_parts = p.max_parts;
+  a.fanout = p.fanout;
+  a.max_nodes = p.max_nodes;
+  return from_hip(launch_paged_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t i8kv_prefix_prefill_workspace_bytes(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                           int32_t total_q) {
+  (void)desc;
+  (void)num_seqs;
+  (void)total_q;
+  return 0;
+}
+
+i8kv_status i8kv_prefix_prefill_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                     int32_t total_q, int32_t max_query_len,
+                                     const int8_t* q_int8, const float* q_scale,
+                                     const int32_t* query_start_loc, const int32_t* seq_lens,
+                                     const int8_t* k_cache, const int8_t* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     int32_t w_group, float softmax_scale, void* workspace,
+                                     size_t workspace_bytes, float* out,
+                                     i8kv_stream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  i8kv_status st = check_desc(desc);
+  if (st != I8KV_OK) return st;
+  if (!q_int8 || !q_scale || !query_start_loc || !seq_lens || !k_cache || !v_cache ||
+      !k_scale || !v_scale || !block_tables || !out)
+    return I8KV_ERR_NULL;
+  if (num_seqs < 0 || total_q < 0 || max_query_len < 0 || max_blocks_per_seq <= 0)
+    return I8KV_ERR_INVALID_ARG;
+  if (max_query_len > total_q) return I8KV_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return I8KV_ERR_INVALID_ARG;
+  if (w_group != 32 && w_group != 64) return I8KV_ERR_UNSUPPORTED;
+  if (num_seqs > kMaxGridYZ) return I8KV_ERR_UNSUPPORTED;
+  if (!aligned16(q_int8) || !aligned16(k_cache) || !aligned16(v_cache))
+    return I8KV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q == 0) return I8KV_OK;
+  PrefillArgs a{};
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.max_query_len = max_query_len;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.group = desc->num_q_heads / desc->num_kv_heads;
+  a.head_dim = desc->head_dim;
+  a.num_blocks = desc->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.w_group = w_group;
+  a.softmax_scale = softmax_scale;
+  a.q_int8 = q_int8;
+  a.q_scale = q_scale;
+  a.query_start_loc = query_start_loc;
+  a.seq_lens = seq_lens;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.out = out;
+  return from_hip(launch_prefix_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

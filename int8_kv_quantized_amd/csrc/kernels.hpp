@@ -1,0 +1,85 @@
+// Internal launch interface between the C ABI (abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace i8kv {
+
+constexpr int kBlockSize = 16;   // tokens per page
+constexpr int kPartition = 256;  // decode partition (tokens)
+
+struct ProducerArgs {
+  int32_t num_tokens, num_q_heads, num_kv_heads, head_dim, num_blocks;
+  const uint16_t* key;
+  const uint16_t* value;
+  const uint16_t* query;  // may be null
+  int8_t* q_int8;
+  float* q_scale;
+  const int32_t* slot_mapping;
+  int8_t* k_cache;
+  int8_t* v_cache;
+  float* k_scale;
+  float* v_scale;
+};
+
+hipError_t launch_kv_quantize_write(const ProducerArgs& a, hipStream_t stream);
+
+// Decode workspace: per-partition partials, per-group partials and counters.
+struct DecodePlan {
+  int32_t num_seqs, num_kv_heads, group;  // group = Hq / Hkv
+  int32_t head_dim;
+  int32_t max_parts;    // ceil(max_seq_len / 256)
+  int32_t fanout;       // partitions merged per first-level node
+  int32_t max_nodes;    // ceil(max_parts / fanout)
+  size_t off_part_o, off_part_ml, off_node_o, off_node_ml, off_cnt1, off_cnt2, bytes;
+};
+
+DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t group,
+                            int32_t head_dim, int32_t max_seq_len);
+
+struct DecodeArgs {
+  int32_t num_seqs, num_q_heads, num_kv_heads, group, head_dim, num_blocks;
+  int32_t max_blocks_per_seq, max_seq_len, w_group;
+  float softmax_scale;
+  const int8_t* q_int8;
+  const float* q_scale;
+  const int8_t* k_cache;
+  const int8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* out;
+  // workspace views
+  float* part_o;    // [S, Hkv, max_parts, group, D]
+  float* part_ml;   // [S, Hkv, max_parts, group, 2]
+  float* node_o;    // [S, Hkv, max_nodes, group, D]
+  float* node_ml;   // [S, Hkv, max_nodes, group, 2]
+  int32_t* cnt1;    // [S, Hkv, max_nodes]
+  int32_t* cnt2;    // [S, Hkv]
+  int32_t max_parts, fanout, max_nodes;
+};
+
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  int32_t num_seqs, total_q, max_query_len, num_q_heads, num_kv_heads, group, head_dim,
+      num_blocks, max_blocks_per_seq, w_group;
+  float softmax_scale;
+  const int8_t* q_int8;
+  const float* q_scale;
+  const int32_t* query_start_loc;
+  const int32_t* seq_lens;
+  const int8_t* k_cache;
+  const int8_t* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  float* out;
+};
+
+hipError_t launch_prefix_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace i8kv

@@ -18,3 +18,11 @@ def pytest_configure(config):
 def orc():
     import oracle
     return oracle.default()
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_test(request):
+    """Name each GPU test on stdout before it touches the device."""
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu] {request.node.nodeid}", file=sys.__stdout__, flush=True)
+    yield

@@ -1,0 +1,79 @@
+"""Helpers for the GPU parity tests: move a workload to the device, run the
+HIP path through the C ABI, and compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import workloads as W
+
+
+def say(*a):
+    print(*a, file=sys.__stdout__, flush=True)
+
+
+def dev(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def desc_of(wl):
+    import int8_kv_quantized_amd as K
+    return K.CacheDesc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks)
+
+
+def split_tokens(wl):
+    is_q = np.zeros(wl.num_tokens, bool)
+    is_q[wl.query_token_index] = True
+    return np.nonzero(~is_q)[0], wl.query_token_index
+
+
+def gpu_fill(wl):
+    """Producer on the GPU: history tokens without Q, then the query tokens."""
+    import int8_kv_quantized_amd as K
+    d = desc_of(wl)
+    cache = K.PagedCache.allocate(d)
+    hist, qi = split_tokens(wl)
+    if hist.size:
+        K.kv_quantize_write(d, dev(wl.key[hist]), dev(wl.value[hist]),
+                            dev(wl.slot_mapping[hist]), cache)
+    q8, qs = K.kv_quantize_write(d, dev(wl.key[qi]), dev(wl.value[qi]),
+                                 dev(wl.slot_mapping[qi]), cache, query=dev(wl.query))
+    return d, cache, q8, qs
+
+
+def cache_to_np(cache):
+    return dict(k_cache=cache.k_cache.cpu().numpy(), v_cache=cache.v_cache.cpu().numpy(),
+                k_scale=cache.k_scale.cpu().numpy(), v_scale=cache.v_scale.cpu().numpy())
+
+
+def assert_bits_equal(a, b, what):
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    if a.dtype.kind == "f":
+        a, b = a.view(np.uint32), b.view(np.uint32)
+    bad = np.count_nonzero(a != b)
+    assert bad == 0, f"{what}: {bad} of {a.size} elements differ"
+
+
+def assert_close(got, ref, what, max_abs=1e-3, mean_abs=1e-4):
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    mx, mn = float(err.max()), float(err.mean())
+    say(f"    {what}: max-abs {mx:.3e}  mean-abs {mn:.3e}")
+    assert mx <= max_abs and mn <= mean_abs, f"{what}: max-abs {mx:.3e} mean-abs {mn:.3e}"
+    return mx, mn
+
+
+def decode_queries(q8, qs, wl):
+    """Rows of the producer's Q that are the decode queries (newest token)."""
+    rows = wl.decode_query_rows()
+    return q8[rows].contiguous(), qs[rows].contiguous()
+
+
+def report_fp64(got, ref64, what):
+    err = np.abs(got.astype(np.float64) - ref64)
+    say(f"    {what} vs unquantized fp64 attention: max-abs {err.max():.3e} "
+        f"mean-abs {err.mean():.3e}")

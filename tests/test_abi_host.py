@@ -1,0 +1,139 @@
+"""Host-side tests of the C ABI (no GPU needed, nothing is launched).
+
+* libi8kv.so loads and exports every function include/i8kv.h declares;
+* every argument check returns its documented status before any launch
+  (all calls below fail validation, so no kernel is ever enqueued).
+"""
+import ctypes as C
+import re
+from pathlib import Path
+
+import pytest
+
+import int8_kv_quantized_amd as K
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "i8kv.h"
+OK, NULL, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3, 4
+FAKE = 0x100000  # 16-byte aligned stand-in pointer, never dereferenced
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(i8kv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for op in ("i8kv_kv_quantize_write", "i8kv_paged_decode_int8", "i8kv_prefix_prefill_int8"):
+        assert op in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.CDLL(str(K.lib_path()))
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_abi_version_and_status_strings():
+    assert K.abi_version() == 1
+    for st in range(6):
+        assert K.status_string(st)
+    assert K.status_string(99) == "unknown status"
+
+
+def _lib():
+    return K.load_library()
+
+
+def desc(Hq=24, Hkv=4, D=256, nb=64, bs=16):
+    return K.CacheDesc(Hq, Hkv, D, nb, bs)
+
+
+def producer(d, T=4, key=FAKE, value=FAKE, query=None, q8=None, qs=None, slot=FAKE,
+             kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE):
+    P = lambda x: None if x is None else C.c_void_p(x)
+    return _lib().i8kv_kv_quantize_write(None if d is None else C.byref(d), T, P(key), P(value),
+                                        P(query), P(q8), P(qs), P(slot), P(kc), P(vc), P(ks),
+                                        P(vs), None)
+
+
+def decode(d, S=1, max_len=512, max_blocks=32, part=256, G=32, ws=FAKE, ws_bytes=1 << 30,
+           q8=FAKE, out=FAKE, scale=0.0625, bt=FAKE):
+    P = lambda x: None if x is None else C.c_void_p(x)
+    return _lib().i8kv_paged_decode_int8(
+        None if d is None else C.byref(d), S, P(q8), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+        P(bt), max_blocks, P(FAKE), max_len, part, G, scale, P(ws), ws_bytes, P(out), None)
+
+
+def prefill(d, S=1, Tq=8, max_q=8, G=32, q8=FAKE, qsl=FAKE, scale=0.0625):
+    P = lambda x: None if x is None else C.c_void_p(x)
+    return _lib().i8kv_prefix_prefill_int8(
+        None if d is None else C.byref(d), S, Tq, max_q, P(q8), P(FAKE), P(qsl), P(FAKE),
+        P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 32, G, scale, None, 0, P(FAKE), None)
+
+
+# --- producer ---------------------------------------------------------------
+@pytest.mark.parametrize("kw,expect", [
+    (dict(key=None), NULL), (dict(value=None), NULL), (dict(slot=None), NULL),
+    (dict(kc=None), NULL), (dict(vs=None), NULL),
+    (dict(query=FAKE, q8=None, qs=FAKE), NULL), (dict(query=FAKE, q8=FAKE, qs=None), NULL),
+    (dict(T=-1), INVALID), (dict(key=FAKE + 2), INVALID), (dict(kc=FAKE + 8), INVALID),
+    (dict(T=0), OK),
+])
+def test_producer_validation(kw, expect):
+    assert producer(desc(), **kw) == expect
+
+
+@pytest.mark.parametrize("d,expect", [
+    (None, NULL), (desc(D=100), UNSUPPORTED), (desc(D=512), UNSUPPORTED),
+    (desc(bs=32), UNSUPPORTED), (desc(Hq=24, Hkv=5), UNSUPPORTED),
+    (desc(Hq=34, Hkv=2), UNSUPPORTED), (desc(Hq=0), INVALID), (desc(nb=0), INVALID),
+])
+def test_descriptor_validation(d, expect):
+    assert producer(d) == expect
+    assert decode(d) == expect
+    assert prefill(d) == expect
+
+
+# --- decode -------------------------------------------------------------------
+def test_decode_workspace_query():
+    d = desc()
+    small = K.paged_decode_workspace_bytes(d, 1, 512)
+    big = K.paged_decode_workspace_bytes(d, 16, 32768)
+    assert 0 < small < big
+    assert K.paged_decode_workspace_bytes(d, 1, 512, partition_size=512) == 0
+    assert K.paged_decode_workspace_bytes(d, -1, 512) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(S=-1), INVALID), (dict(max_len=-1), INVALID), (dict(max_blocks=0), INVALID),
+    (dict(max_len=16 * 32 + 1), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(part=512), UNSUPPORTED), (dict(G=48), UNSUPPORTED), (dict(G=16), UNSUPPORTED),
+    (dict(max_len=(1 << 20) + 16, max_blocks=1 << 17), UNSUPPORTED),
+    (dict(q8=None), NULL), (dict(bt=None), NULL), (dict(out=None), NULL),
+    (dict(q8=FAKE + 4), INVALID), (dict(out=FAKE + 4), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE), (dict(ws=FAKE + 16), WORKSPACE),
+    (dict(S=0), OK),
+])
+def test_decode_validation(kw, expect):
+    assert decode(desc(), **kw) == expect
+
+
+# --- prefill ------------------------------------------------------------------
+@pytest.mark.parametrize("kw,expect", [
+    (dict(S=-1), INVALID), (dict(Tq=-1), INVALID), (dict(max_q=9), INVALID),
+    (dict(G=16), UNSUPPORTED), (dict(scale=float("inf")), INVALID),
+    (dict(q8=None), NULL), (dict(qsl=None), NULL), (dict(q8=FAKE + 1), INVALID),
+    (dict(S=0), OK), (dict(Tq=0, max_q=0), OK),
+])
+def test_prefill_validation(kw, expect):
+    assert prefill(desc(), **kw) == expect
+
+
+def test_binding_rejects_missing_library(monkeypatch, tmp_path):
+    from int8_kv_quantized_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "HERE", tmp_path)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _binding.load_library()

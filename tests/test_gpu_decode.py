@@ -1,0 +1,109 @@
+"""GPU parity of paged decode against the oracle.
+
+The int8 caches must be bit-identical first (they feed both sides); decode
+outputs must then agree with the oracle within max-abs 1e-3 and mean-abs
+1e-4.  The error against unquantized fp64 attention is reported alongside.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_helpers import (assert_bits_equal, assert_close, cache_to_np, decode_queries, dev,
+                         gpu_fill, report_fp64, say)
+from refmath import decode_reference_fp64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(wl, orc, G, report=True, repeat=2):
+    import int8_kv_quantized_amd as K
+    say(f"  decode case {wl.name}: S={wl.num_seqs} Lmax={wl.max_seq_len} Hq={wl.num_q_heads} "
+        f"Hkv={wl.num_kv_heads} D={wl.head_dim} G={G}")
+    d, cache, q8, qs = gpu_fill(wl)
+    ocache, oq8, oqs = orc.fill(wl)
+    g = cache_to_np(cache)
+    for k in g:
+        assert_bits_equal(g[k], ocache[k], f"{wl.name} {k}")
+    dq8, dqs = decode_queries(q8, qs, wl)
+    bt, sl = dev(wl.block_tables), dev(wl.seq_lens)
+    import torch
+    ws = torch.zeros(max(256, K.paged_decode_workspace_bytes(d, wl.num_seqs, wl.max_seq_len)),
+                     dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(repeat):
+        out = K.paged_decode_int8(d, dq8, dqs, cache, bt, sl, wl.max_seq_len, w_group=G,
+                                  workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    rows = wl.decode_query_rows()
+    ref = orc.paged_decode(oq8[rows], oqs[rows], ocache, wl.block_tables, wl.seq_lens,
+                           num_q_heads=wl.num_q_heads, w_group=G)
+    assert_close(outs[0], ref, f"{wl.name} G={G}")
+    for o in outs[1:]:   # the workspace counters were restored by the first call
+        assert np.array_equal(o, outs[0]), "repeated call differs"
+    if report:
+        report_fp64(outs[0], decode_reference_fp64(wl), f"{wl.name} G={G}")
+    return outs[0], ref
+
+
+SMALL = [
+    dict(name="ragged_d128_g3", seq_lens=(37, 300, 16, 1, 700, 256, 257), num_q_heads=6,
+         num_kv_heads=2, head_dim=128),
+    dict(name="d64_mha", seq_lens=(5, 70, 513), num_q_heads=4, num_kv_heads=4, head_dim=64),
+    dict(name="d256_g6", seq_lens=(33, 1024, 2000), num_q_heads=24, num_kv_heads=4,
+         head_dim=256),
+    dict(name="d256_g16", seq_lens=(40, 4000), num_q_heads=16, num_kv_heads=1, head_dim=256),
+    dict(name="d128_g8_long", seq_lens=(9000,), num_q_heads=8, num_kv_heads=1, head_dim=128),
+]
+
+
+@pytest.mark.parametrize("G", [32, 64])
+@pytest.mark.parametrize("kw", SMALL, ids=lambda k: k["name"])
+def test_decode_small(orc, kw, G):
+    kw = dict(kw)
+    name = kw.pop("name")
+    wl = W.make_workload(name, new_tokens=[1] * len(kw["seq_lens"]), seed=51, w_group=G, **kw)
+    run_decode(wl, orc, G)
+
+
+def test_decode_empty_sequence(orc):
+    import int8_kv_quantized_amd as K
+    import torch
+    wl = W.make_workload("empty", seq_lens=[20, 300], new_tokens=[1, 1], num_q_heads=6,
+                         num_kv_heads=2, head_dim=128, seed=52)
+    say("  decode case empty: one sequence of length 0")
+    d, cache, q8, qs = gpu_fill(wl)
+    dq8, dqs = decode_queries(q8, qs, wl)
+    lens = np.array([0, 300], np.int32)
+    out = K.paged_decode_int8(d, dq8, dqs, cache, dev(wl.block_tables), dev(lens), 300)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ocache, oq8, oqs = orc.fill(wl)
+    rows = wl.decode_query_rows()
+    ref = orc.paged_decode(oq8[rows], oqs[rows], ocache, wl.block_tables, lens, num_q_heads=6)
+    assert not out[0].any()
+    assert_close(out, ref, "empty")
+
+
+@pytest.mark.parametrize("G", [32])
+def test_decode_cfg1_L512(orc, G):
+    run_decode(W.cfg1_decode_512(G), orc, G)
+
+
+@pytest.mark.parametrize("G", [32, 64])
+@pytest.mark.parametrize("L", [4096, 8192, 16384])
+def test_decode_cfg2_outlier_v(orc, L, G):
+    run_decode(W.cfg2_decode(L, G), orc, G)
+
+
+def test_decode_cfg3_32k(orc):
+    run_decode(W.cfg3_decode_32k(), orc, 32)
+
+
+def test_decode_cfg3_batch16(orc):
+    run_decode(W.cfg3_decode_batch16(), orc, 32, report=False)
+
+
+@pytest.mark.parametrize("G", [32, 64])
+def test_decode_cfg5_mha(orc, G):
+    run_decode(W.cfg5_mha_producer_decode(G), orc, G)
