@@ -95,8 +95,8 @@ i8kv_status i8kv_kv_quantize_write(const i8kv_cache_desc* desc, int32_t num_toke
 
 /*
  * Bytes of device workspace that i8kv_paged_decode_int8 needs for num_seqs
- * sequences of at most max_seq_len tokens: per-partition (m, l, output)
- * partials plus merge counters.  Returns 0 for invalid arguments.
+ * sequences of at most max_seq_len tokens: the per-partition partials
+ * (m_p, l_p and the partition output).  Returns 0 for invalid arguments.
  */
 size_t i8kv_paged_decode_workspace_bytes(const i8kv_cache_desc* desc, int32_t num_seqs,
                                          int32_t max_seq_len, int32_t partition_size);
@@ -114,13 +114,13 @@ size_t i8kv_paged_decode_workspace_bytes(const i8kv_cache_desc* desc, int32_t nu
  *   q_int8 [S, Hq, D], q_scale [S, Hq]   (as written by the producer)
  *   block_tables [S, max_blocks_per_seq] int32, seq_lens [S] int32
  *   out [S, Hq, D] fp32, fully overwritten (seq_len 0 gives zeros)
- * workspace: device memory of at least
+ * workspace: device memory (256-byte aligned) of at least
  *   i8kv_paged_decode_workspace_bytes(desc, S, max_seq_len, partition_size)
- *   bytes, zero-filled once by the caller when it is allocated; every call
- *   leaves its counters at zero again.  Calls that run concurrently must use
- *   different workspaces.
+ *   bytes; its contents need no initialization.  Calls that run concurrently
+ *   must use different workspaces.  The call enqueues two kernels (partitions,
+ *   then the merge, skipped when no sequence spans more than one partition).
  * Errors: NULL, INVALID_ARG (S < 0, max_seq_len < 0, max_seq_len larger than
- * 16 * max_blocks_per_seq), UNSUPPORTED, WORKSPACE.
+ * 16 * max_blocks_per_seq), UNSUPPORTED (also max_seq_len > 2^20), WORKSPACE.
  */
 i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
                                    const int8_t* q_int8, const float* q_scale,

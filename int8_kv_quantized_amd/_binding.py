@@ -221,7 +221,7 @@ def paged_decode_int8(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block
     """Paged decode over the int8 cache; returns ``out`` [S, Hq, D] fp32.
 
     ``workspace`` must hold paged_decode_workspace_bytes(...) bytes and be
-    zero-filled when first allocated (allocated and zeroed here if None).
+    256-byte aligned (allocated here if None; contents need no initialization).
     """
     import torch
     lib = load_library()

@@ -8,6 +8,7 @@ from pathlib import Path
 
 HERE = Path(__file__).resolve().parent
 CSRC = HERE / "csrc"
+INCLUDE = HERE.parent / "include"
 LIB = HERE / "libi8kv.so"
 SOURCES = ["abi.hip", "producer.hip", "decode.hip", "prefill.hip"]
 
@@ -33,7 +34,8 @@ def hipcc() -> str:
 def build(out: Path = LIB, extra=()) -> Path:
     out = Path(out)
     tmp = out.with_suffix(out.suffix + f".tmp{os.getpid()}")
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, *[str(CSRC / s) for s in SOURCES], "-o", str(tmp)]
+    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", *extra, *[str(CSRC / s) for s in SOURCES],
+           "-o", str(tmp)]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

@@ -6,14 +6,14 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/i8kv.h"
+#include "i8kv.h"
 #include "kernels.hpp"
 
 namespace {
 
 using namespace i8kv;
 
-constexpr int32_t kMaxSeqLen = 1 << 20;  // 4096 partitions: 64 x 64 merge tree
+constexpr int32_t kMaxSeqLen = 1 << 20;  // at most 4096 decode partitions
 constexpr int32_t kMaxGridYZ = 65535;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -150,13 +150,7 @@ i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs
   a.out = out;
   a.part_o = reinterpret_cast<float*>(ws + p.off_part_o);
   a.part_ml = reinterpret_cast<float*>(ws + p.off_part_ml);
-  a.node_o = reinterpret_cast<float*>(ws + p.off_node_o);
-  a.node_ml = reinterpret_cast<float*>(ws + p.off_node_ml);
-  a.cnt1 = reinterpret_cast<int32_t*>(ws + p.off_cnt1);
-  a.cnt2 = reinterpret_cast<int32_t*>(ws + p.off_cnt2);
   a.max_parts = p.max_parts;
-  a.fanout = p.fanout;
-  a.max_nodes = p.max_nodes;
   return from_hip(launch_paged_decode(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -27,31 +27,145 @@ __device__ __forceinline__ int quantize_code(float x, float s) {
   return (int)r;
 }
 
-// Butterfly reductions inside aligned groups of `width` lanes (width <= 64).
+// Code of an already divided value: clamp(round(q), -127, 127).
+__device__ __forceinline__ int round_code(float q) {
+  return (int)fminf(fmaxf(roundf(q), -127.0f), 127.0f);
+}
+
+// The IEEE fp32 quotient a / b from rb = 1/b rounded to fp64.  The quotient
+// of two fp32 values is never an fp32 rounding midpoint and lies at least
+// about 2^-50 (relative) away from one, while a * rb carries a relative error
+// below 2^-52, so rounding it to fp32 gives the correctly rounded quotient.
+__device__ __forceinline__ float div_f32_rn(float a, double rb) {
+  return (float)((double)a * rb);
+}
+
+// ---- cross-lane reductions inside aligned groups of `width` lanes ----------
+// Within a 16-lane row: DPP quad_perm [1,0,3,2] and [2,3,0,1] (pairs at
+// distance 1 and 2), row_half_mirror (lane i <-> 7-i of each 8) and
+// row_mirror (i <-> 15-i): after each step every lane holds the reduction of
+// its block, and the mirrors pair the two halves of the next larger block.
+// Across rows: v_permlane16_swap / v_permlane32_swap return, for every lane,
+// its own value and its partner's (rows 2k <-> 2k+1, halves), so op(r0, r1)
+// completes the next level whichever of the two is the partner.
+enum : int { kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
+
+template <int ctrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, false);
+}
+
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct AddOp {
+  __device__ float operator()(float a, float b) const { return a + b; }
+  __device__ double operator()(double a, double b) const { return a + b; }
+};
+
+__device__ __forceinline__ float bits_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t f_bits(float f) { return __float_as_uint(f); }
+
+template <int ctrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return bits_f(dpp_u32<ctrl>(f_bits(v)));
+}
+template <int ctrl>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = dpp_u32<ctrl>((uint32_t)u), hi = dpp_u32<ctrl>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ void swap16(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap32(uint32_t v, uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+template <int width, typename Op>
+__device__ __forceinline__ float group_reduce(float v, Op op) {
+  if constexpr (width >= 2) v = op(v, dpp_f<kDppXor1>(v));
+  if constexpr (width >= 4) v = op(v, dpp_f<kDppXor2>(v));
+  if constexpr (width >= 8) v = op(v, dpp_f<kDppHalfMirror>(v));
+  if constexpr (width >= 16) v = op(v, dpp_f<kDppMirror>(v));
+  if constexpr (width >= 32) {
+    uint32_t a, b;
+    swap16(f_bits(v), a, b);
+    v = op(bits_f(a), bits_f(b));
+  }
+  if constexpr (width >= 64) {
+    uint32_t a, b;
+    swap32(f_bits(v), a, b);
+    v = op(bits_f(a), bits_f(b));
+  }
+  return v;
+}
+
+template <int width>
+__device__ __forceinline__ double group_reduce_sum(double v) {
+  if constexpr (width >= 2) v += dpp_d<kDppXor1>(v);
+  if constexpr (width >= 4) v += dpp_d<kDppXor2>(v);
+  if constexpr (width >= 8) v += dpp_d<kDppHalfMirror>(v);
+  if constexpr (width >= 16) v += dpp_d<kDppMirror>(v);
+  if constexpr (width >= 32) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    uint32_t la, lb, ha, hb;
+    swap16((uint32_t)u, la, lb);
+    swap16((uint32_t)(u >> 32), ha, hb);
+    v = __longlong_as_double((long long)(((uint64_t)ha << 32) | la)) +
+        __longlong_as_double((long long)(((uint64_t)hb << 32) | lb));
+  }
+  if constexpr (width >= 64) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    uint32_t la, lb, ha, hb;
+    swap32((uint32_t)u, la, lb);
+    swap32((uint32_t)(u >> 32), ha, hb);
+    v = __longlong_as_double((long long)(((uint64_t)ha << 32) | la)) +
+        __longlong_as_double((long long)(((uint64_t)hb << 32) | lb));
+  }
+  return v;
+}
+
 template <int width>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return group_reduce<width>(v, MaxOp{});
 }
-
-template <int width>
-__device__ __forceinline__ double group_sum(double v) {
-#pragma unroll
-  for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
 template <int width>
 __device__ __forceinline__ float group_sumf(float v) {
-#pragma unroll
-  for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return group_reduce<width>(v, AddOp{});
+}
+template <int width>
+__device__ __forceinline__ double group_sum(double v) {
+  return group_reduce_sum<width>(v);
 }
 
-// Correctly rounded fp32 exponential: e^x evaluated in fp64 and rounded once.
+// fp32 exponential rounded once from an fp64 evaluation of e^x (relative
+// error about 2^-42 before the final rounding, so the fp32 result is the
+// correctly rounded one except within ~2^-18 of a rounding midpoint).
+// Method: e^x = 2^t with t = x log2(e); t = n + f, n = rint(t), |f| <= 1/2;
+// 2^f = e^(f ln 2) by its Taylor series to degree 10 (Horner); scale by 2^n.
 __device__ __forceinline__ float exp_f32_rn(float x) {
-  return (float)exp((double)x);
+  const double t = (double)x * 1.4426950408889634074;
+  const double n = __builtin_rint(t);
+  const double g = (t - n) * 0.69314718055994530942;
+  double p = 2.7557319223985893e-07;          // 1/10!
+  p = __builtin_fma(p, g, 2.7557319223985888e-06);  // 1/9!
+  p = __builtin_fma(p, g, 2.4801587301587302e-05);  // 1/8!
+  p = __builtin_fma(p, g, 1.9841269841269841e-04);  // 1/7!
+  p = __builtin_fma(p, g, 1.3888888888888889e-03);  // 1/6!
+  p = __builtin_fma(p, g, 8.3333333333333333e-03);  // 1/5!
+  p = __builtin_fma(p, g, 4.1666666666666667e-02);  // 1/4!
+  p = __builtin_fma(p, g, 1.6666666666666667e-01);  // 1/3!
+  p = __builtin_fma(p, g, 0.5);
+  p = __builtin_fma(p, g, 1.0);
+  p = __builtin_fma(p, g, 1.0);
+  return (float)__builtin_ldexp(p, (int)n);
 }
 
 }  // namespace i8kv

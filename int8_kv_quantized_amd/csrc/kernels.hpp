@@ -26,14 +26,12 @@ struct ProducerArgs {
 
 hipError_t launch_kv_quantize_write(const ProducerArgs& a, hipStream_t stream);
 
-// Decode workspace: per-partition partials, per-group partials and counters.
+// Decode workspace: per-partition partial outputs and (m, l).
 struct DecodePlan {
   int32_t num_seqs, num_kv_heads, group;  // group = Hq / Hkv
   int32_t head_dim;
   int32_t max_parts;    // ceil(max_seq_len / 256)
-  int32_t fanout;       // partitions merged per first-level node
-  int32_t max_nodes;    // ceil(max_parts / fanout)
-  size_t off_part_o, off_part_ml, off_node_o, off_node_ml, off_cnt1, off_cnt2, bytes;
+  size_t off_part_o, off_part_ml, bytes;
 };
 
 DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t group,
@@ -55,11 +53,7 @@ struct DecodeArgs {
   // workspace views
   float* part_o;    // [S, Hkv, max_parts, group, D]
   float* part_ml;   // [S, Hkv, max_parts, group, 2]
-  float* node_o;    // [S, Hkv, max_nodes, group, D]
-  float* node_ml;   // [S, Hkv, max_nodes, group, 2]
-  int32_t* cnt1;    // [S, Hkv, max_nodes]
-  int32_t* cnt2;    // [S, Hkv]
-  int32_t max_parts, fanout, max_nodes;
+  int32_t max_parts;
 };
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);

@@ -7,27 +7,32 @@
 //   section 2.1 state (m, l, o): m' = max(m, max s), alpha = exp(m - m'),
 //               p~ = exp(s - m'), W = p~ * sV quantized per G-key group,
 //               o = alpha o + sum sW (Wq x Vq), l = alpha l + sum p~, O = o / l;
-//   section 3/4 W is operand A, V operand B, one scale per group of exactly
-//               the keys one MFMA chain consumes;
+//   section 3/4 W and V are the two int8 operands of the PV product; one
+//               scale per group of exactly the keys one MFMA (chain) consumes;
 // and "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
 // DCU", section 3.2 (history and chunk in the same online softmax) and
-// section 4.2 (more query rows per workgroup so each K/V tile is reused).
+// section 4.2 (many query rows per workgroup so each K/V tile is reused).
 //
-// gfx950 mapping.  A workgroup of 4 waves owns 128 consecutive flattened rows
-// (query token, q head of the GQA group) of one (sequence, KV head); wave w
-// owns rows 32w..32w+31, lane l (and its partner l^32) row l%32.  Per 64-key
-// tile, K and V pages are staged in LDS in their cache layouts.
-//  * QK is computed transposed, S^T = K Q^T, with v_mfma_i32_32x32x32_i8:
-//    operand A = 32 keys (16 head-dim bytes per lane from LDS), operand B =
-//    the int8 queries (held in registers for the whole loop).  The A rows are
-//    a permutation of the keys chosen so that output register v of lane l is
-//    key 16*(l/32) + v: each lane holds 16 consecutive keys of its row.
-//  * Those 16 keys are exactly the operand-A slice of the PV MFMA
-//    (v_mfma_i32_32x32x32_i8, K = 32 keys): W is quantized and packed in
-//    registers and never leaves them.  Operand B is V straight from the LDS
-//    copy of the page (16 tokens of one dim are 16 contiguous bytes).
-//  * G = 32: one PV MFMA per 32-key group and 32 output dims, rescaled by the
-//    group's sW.  G = 64: two MFMAs chained in int32 (same scale), one rescale.
+// gfx950 mapping.  A workgroup of 12 waves owns 192 consecutive flattened
+// rows (query token, q head of the GQA group) of one (sequence, KV head) --
+// 32 tokens x 6 heads for Qwen-like 24/4 heads; wave w owns 16 rows and lane
+// l row l%16 (the four lanes l%16 + 16j share a row).  K/V tiles of 64 keys
+// are staged in LDS in their page layouts.
+//  * QK, transposed: S^T = K Q^T with v_mfma_i32_16x16x64_i8 (operand A = 16
+//    keys x 64 head-dim bytes from LDS, operand B = the int8 queries held in
+//    registers).  Two MFMA chains per 32-key group; their A rows read keys
+//    8(r/4) + 4b + r%4, so output register i of lane l in chain b is key
+//    8(l/16) + 4b + i: each lane ends with 8 consecutive keys of its row.
+//  * PV, also transposed: O^T = V^T Wq^T with v_mfma_i32_16x16x32_i8 (K = 32
+//    keys = one group for G = 32; two chained MFMAs for G = 64).  Operand B
+//    is Wq^T, whose lane slice is exactly the 8 keys the lane already holds;
+//    operand A is V^T, 8 tokens of one dim from the LDS copy of the page.  The
+//    output O^T keeps lane l on row l%16, so sW, alpha and l are per-lane
+//    scalars and the group rescale O += sW * float(C) needs no exchange.
+//  * Online softmax in base 2 (log2 e folded into the per-row constant);
+//    the output is rescaled only when the running max grows by more than 8
+//    (p~ stays below 2^8), which is exact in real arithmetic since Wq and O
+//    do not depend on the reference max.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -35,36 +40,44 @@ namespace i8kv {
 
 namespace {
 
-constexpr int kNW = 4;         // waves per workgroup
-constexpr int kRows = 32 * kNW;  // flattened rows per workgroup
-constexpr int kKT = 64;        // keys per tile
+constexpr int kNW = 12;            // waves per workgroup
+constexpr int kRows = 16 * kNW;    // flattened rows per workgroup
+constexpr int kKT = 64;            // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;      // rescale threshold (log2 units)
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Reduce over the four lanes that share a row (lanes r, r+16, r+32, r+48).
+__device__ __forceinline__ float row_max4(float v) {
+  uint32_t a, b;
+  swap16(f_bits(v), a, b);
+  v = fmaxf(bits_f(a), bits_f(b));
+  swap32(f_bits(v), a, b);
+  return fmaxf(bits_f(a), bits_f(b));
 }
-
-// A-row r of the transposed QK reads key perm(r) so that output register v
-// of lane l holds key 16*(l/32) + v.
-__device__ __forceinline__ int key_of_arow(int r) {
-  const int j = r >> 3, h = (r >> 2) & 1, i = r & 3;
-  return 16 * h + 4 * j + i;
+__device__ __forceinline__ float row_sum4(float v) {
+  uint32_t a, b;
+  swap16(f_bits(v), a, b);
+  v = bits_f(a) + bits_f(b);
+  swap32(f_bits(v), a, b);
+  return bits_f(a) + bits_f(b);
 }
 
 }  // namespace
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void prefix_prefill_kernel(PrefillArgs a) {
-  constexpr int NC = D / 32;  // 32-dim k-steps (QK) and 32-dim output tiles (PV)
-  __shared__ __attribute__((aligned(16))) int8_t s_k[D / 16][kKT][16];
+__global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs a) {
+  constexpr int NC = D / 64;   // 64-dim k-steps of QK
+  constexpr int NN = D / 16;   // 16-dim output tiles of PV
+  constexpr int NT = kNW * kWave;
+  // LDS tiles in page layout: K [page][chunk][key][16 B], V [page][dim][16 B]
+  __shared__ __attribute__((aligned(16))) int8_t s_k[kKT / 16][D / 16][16][16];
   __shared__ __attribute__((aligned(16))) int8_t s_v[kKT / 16][D][16];
-  __shared__ float s_sk[kKT], s_sv[kKT];
-  __shared__ __attribute__((aligned(16))) float s_row[kNW][32];
+  __shared__ __attribute__((aligned(16))) float s_sk[kKT];
+  __shared__ __attribute__((aligned(16))) float s_sv[kKT];
   __shared__ int s_pid[kKT / 16];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int hl = lane >> 5, rl = lane & 31;
+  const int lg = lane >> 4, lr = lane & 15;
   const int s = blockIdx.z, kv = blockIdx.y;
   const int grp = a.group, Hkv = a.num_kv_heads;
 
@@ -77,7 +90,7 @@ __global__ __launch_bounds__(256) void prefix_prefill_kernel(PrefillArgs a) {
   if (row0 >= nrows_seq || ctx < 0) return;
 
   // this lane's row
-  const int fr = row0 + 32 * w + rl;
+  const int fr = row0 + 16 * w + lr;
   const bool row_ok = fr < nrows_seq;
   const int tok = row_ok ? fr / grp : 0;
   const int head = row_ok ? fr % grp : 0;
@@ -87,26 +100,28 @@ __global__ __launch_bounds__(256) void prefix_prefill_kernel(PrefillArgs a) {
   v4i qb[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
-    qb[c] = row_ok ? *reinterpret_cast<const v4i*>(a.q_int8 + qrow * D + 32 * c + 16 * hl)
+    qb[c] = row_ok ? *reinterpret_cast<const v4i*>(a.q_int8 + qrow * D + 64 * c + 16 * lg)
                    : v4i{0, 0, 0, 0};
-  const float sq = row_ok ? a.q_scale[qrow] : 0.0f;
+  // score in log2 units: s2 = acc * sK * (sQ * softmax_scale * log2 e)
+  const float crow = row_ok ? a.q_scale[qrow] * a.softmax_scale * kLog2e : 0.0f;
 
   const int last_fr = min(row0 + kRows, nrows_seq) - 1;
   const int nkeys = ctx + last_fr / grp + 1;  // keys visible to the workgroup's last row
-  const int wave_last_fr = min(row0 + 32 * w + 31, nrows_seq - 1);
-  const int wave_nkeys = (wave_last_fr >= row0 + 32 * w) ? ctx + wave_last_fr / grp + 1 : 0;
+  const int wave_first_fr = row0 + 16 * w;
+  const int wave_last_fr = min(wave_first_fr + 15, nrows_seq - 1);
+  const bool wave_live = wave_first_fr < nrows_seq;
+  const int wave_nkeys = wave_live ? ctx + wave_last_fr / grp + 1 : 0;
+  const int wave_min_pos = wave_live ? ctx + wave_first_fr / grp : 0;
   const int ntiles = (nkeys + kKT - 1) / kKT;
   const int npages_seq = min((seq_len + kBlockSize - 1) / kBlockSize, a.max_blocks_per_seq);
 
-  float m = -INFINITY;
-  float lpart = 0.0f;
-  float O[NC][16];
+  float mref = -INFINITY;  // reference max (log2 units) of this row
+  float lsum = 0.0f;       // this lane's share of l
+  float O[NN][4];
 #pragma unroll
-  for (int n = 0; n < NC; ++n)
+  for (int n = 0; n < NN; ++n)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) O[n][v] = 0.0f;
-
-  const int arow_key = key_of_arow(rl);
+    for (int i = 0; i < 4; ++i) O[n][i] = 0.0f;
 
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * kKT;
@@ -121,24 +136,19 @@ __global__ __launch_bounds__(256) void prefix_prefill_kernel(PrefillArgs a) {
       s_pid[tid] = pid;
     }
     __syncthreads();
-    // K: 4 pages x D/16 chunks x 16 keys, 16 bytes each
-    for (int u = tid; u < 4 * D; u += blockDim.x) {
-      const int i = u / D, rem = u % D, ch = rem / 16, key = rem % 16;
+    // K and V pages of the tile: 4 x (D*16) bytes each, 16 bytes per thread-step
+    constexpr int kUnits = kKT / 16 * D;  // 16-byte units per tile and operand
+    for (int u = tid; u < 2 * kUnits; u += NT) {
+      const int isv = u >= kUnits;
+      const int uu = isv ? u - kUnits : u;
+      const int i = uu / D, rem = uu % D;
       const int pid = s_pid[i];
       v4i val = {0, 0, 0, 0};
-      if (pid >= 0)
-        val = *reinterpret_cast<const v4i*>(
-            a.k_cache + (((size_t)pid * Hkv + kv) * (D / 16) + ch) * 256 + key * 16);
-      *reinterpret_cast<v4i*>(&s_k[ch][16 * i + key][0]) = val;
-    }
-    // V: 4 pages x D dims, 16 tokens each
-    for (int u = tid; u < 4 * D; u += blockDim.x) {
-      const int i = u / D, d = u % D;
-      const int pid = s_pid[i];
-      v4i val = {0, 0, 0, 0};
-      if (pid >= 0)
-        val = *reinterpret_cast<const v4i*>(a.v_cache + (((size_t)pid * Hkv + kv) * D + d) * 16);
-      *reinterpret_cast<v4i*>(&s_v[i][d][0]) = val;
+      const int8_t* src = (isv ? a.v_cache : a.k_cache) + ((size_t)pid * Hkv + kv) * (size_t)D * 16 +
+                          (size_t)rem * 16;
+      if (pid >= 0) val = *reinterpret_cast<const v4i*>(src);
+      int8_t* dst = isv ? &s_v[i][rem][0] : &s_k[i][rem / 16][rem % 16][0];
+      *reinterpret_cast<v4i*>(dst) = val;
     }
     if (tid < kKT) {
       const int key = k0 + tid;
@@ -153,150 +163,130 @@ __global__ __launch_bounds__(256) void prefix_prefill_kernel(PrefillArgs a) {
       s_sv[tid] = svv;
     }
     __syncthreads();
-    if (k0 >= wave_nkeys) continue;  // this wave's rows see no key of the tile
+    if (k0 >= wave_nkeys) continue;  // no key of this tile is visible to the wave
+    const bool diag = k0 + kKT - 1 > wave_min_pos;  // some key may be masked
 
-    // ---- S^T = K Q^T for the two 32-key halves --------------------------
-    float sc[2][16];
+    // ---- S^T = K Q^T: per 32-key group g, two chains of D/64 MFMAs ---------
+    float u2[2][8];  // [group][key 8lg + j]: acc * sK, -inf when masked
     float mt = -INFINITY;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      v16i acc = {};
+    for (int g = 0; g < 2; ++g) {
+      v4i acc[2];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const v4i ka = *reinterpret_cast<const v4i*>(&s_k[2 * c + hl][32 * kh + arow_key][0]);
-        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qb[c], acc, 0, 0, 0);
+      for (int b = 0; b < 2; ++b) {
+        acc[b] = v4i{0, 0, 0, 0};
+        const int krow = 32 * g + 8 * (lr >> 2) + 4 * b + (lr & 3);  // key of A row lr
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const v4i ka =
+              *reinterpret_cast<const v4i*>(&s_k[krow >> 4][4 * c + lg][krow & 15][0]);
+          acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qb[c], acc[b], 0, 0, 0);
+        }
       }
+      const float4 sk0 = *reinterpret_cast<const float4*>(&s_sk[32 * g + 8 * lg]);
+      const float4 sk1 = *reinterpret_cast<const float4*>(&s_sk[32 * g + 8 * lg + 4]);
+      const float skv[8] = {sk0.x, sk0.y, sk0.z, sk0.w, sk1.x, sk1.y, sk1.z, sk1.w};
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int kl = 32 * kh + 16 * hl + v;
-        const int key = k0 + kl;
-        float x = (float)acc[v] * sq;
-        x = x * s_sk[kl];
-        x = x * a.softmax_scale;
-        x = (row_ok && key <= pos) ? x : -INFINITY;
-        sc[kh][v] = x;
+      for (int j = 0; j < 8; ++j) {
+        float x = (float)acc[j >> 2][j & 3] * skv[j];
+        if (diag) {
+          const int key = k0 + 32 * g + 8 * lg + j;
+          x = (row_ok && key <= pos) ? x : -INFINITY;
+        }
+        u2[g][j] = x;
         mt = fmaxf(mt, x);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    const float m_new = fmaxf(m, mt);
-    const float alpha = (m_new == -INFINITY) ? 1.0f : expf(m - m_new);
-    m = m_new;
-
-    // ---- p~, l, W and its group quantization -----------------------------
-    v4i wq[2];
-    float swh[2];
-    float psum = 0.0f;
-    float Wt[2][16];
+    // ---- online softmax (base 2, lazy rescale) -----------------------------
+    mt = row_max4(mt) * crow;  // crow > 0: max of the scaled scores
+    if (!row_ok) mt = -INFINITY;
+    const bool grow = mt > mref + kLazy || mref == -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(grow && mt != -INFINITY)) {
+      const float mnew = (grow && mt != -INFINITY) ? mt : mref;
+      const float alpha = (mref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mref - mnew);
+      if (mnew != mref) {
+        lsum *= alpha;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+        for (int n = 0; n < NN; ++n)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pt = (sc[kh][v] == -INFINITY) ? 0.0f : expf(sc[kh][v] - m_new);
-        psum += pt;
-        Wt[kh][v] = pt * s_sv[32 * kh + 16 * hl + v];
+          for (int i = 0; i < 4; ++i) O[n][i] *= alpha;
+        mref = mnew;
       }
-    lpart = alpha * lpart + psum;
+    }
+    // p~ = 2^(s2 - mref), W = p~ sV, Wq = round(W * 127 / max W)
+    uint32_t wpk[2][2];
+    float swg[2];
     float am[2];
+    float Wv[2][8];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      float x = 0.0f;
+    for (int g = 0; g < 2; ++g) {
+      const float4 sv0 = *reinterpret_cast<const float4*>(&s_sv[32 * g + 8 * lg]);
+      const float4 sv1 = *reinterpret_cast<const float4*>(&s_sv[32 * g + 8 * lg + 4]);
+      const float svv[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};
+      float mx = 0.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) x = fmaxf(x, Wt[kh][v]);
-      am[kh] = fmaxf(x, __shfl_xor(x, 32, kWave));
+      for (int j = 0; j < 8; ++j) {
+        const float pt =
+            row_ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(u2[g][j], crow, -mref)) : 0.0f;
+        lsum += pt;
+        Wv[g][j] = pt * svv[j];
+        mx = fmaxf(mx, Wv[g][j]);
+      }
+      am[g] = row_max4(mx);
     }
     if constexpr (G == 64) am[0] = am[1] = fmaxf(am[0], am[1]);
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const float sw = am[kh] > 0.0f ? am[kh] / 127.0f : 0.0f;
-      swh[kh] = sw;
-      uint32_t pk[4] = {0, 0, 0, 0};
-      if (am[kh] > 0.0f) {
+    for (int g = 0; g < 2; ++g) {
+      swg[g] = am[g] * (1.0f / 127.0f);
+      const float inv = am[g] > 0.0f ? 127.0f * __builtin_amdgcn_rcpf(am[g]) : 0.0f;
+      uint32_t pk[2] = {0, 0};
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          pk[v / 4] |= (uint32_t)(quantize_code(Wt[kh][v], sw) & 0xff) << (8 * (v % 4));
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t q = min((uint32_t)__builtin_fmaf(Wv[g][j], inv, 0.5f), 127u);
+        pk[j >> 2] |= q << (8 * (j & 3));
       }
-      wq[kh] = v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+      wpk[g][0] = pk[0];
+      wpk[g][1] = pk[1];
     }
-
-    // ---- rescale O by alpha of each output row -------------------------------
-    // PV output register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4.
-    if (hl == 0) s_row[w][rl] = alpha;
-    wave_lds_sync();
-    float arow[16];
+    // ---- O^T += sW * (V^T Wq^T) ------------------------------------------------
+    const int vpage_off = 8 * (lg & 1);
+    if constexpr (G == 32) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 q4 = *reinterpret_cast<const float4*>(&s_row[w][8 * j + 4 * hl]);
-      arow[4 * j + 0] = q4.x;
-      arow[4 * j + 1] = q4.y;
-      arow[4 * j + 2] = q4.z;
-      arow[4 * j + 3] = q4.w;
-    }
-    wave_lds_sync();
+      for (int g = 0; g < 2; ++g) {
+        const long wb = (long)(((uint64_t)wpk[g][1] << 32) | wpk[g][0]);
+        const int vpg = 2 * g + (lg >> 1);
 #pragma unroll
-    for (int n = 0; n < NC; ++n)
+        for (int n = 0; n < NN; ++n) {
+          const long va = *reinterpret_cast<const long*>(&s_v[vpg][16 * n + lr][vpage_off]);
+          const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(va, wb, v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) O[n][v] *= arow[v];
-
-    // ---- PV: int8 MFMA per group, rescaled by sW of each row ----------------
-    constexpr int NG = (G == 32) ? 2 : 1;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      if (hl == 0) s_row[w][rl] = swh[g];
-      wave_lds_sync();
-      float srow[16];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 q4 = *reinterpret_cast<const float4*>(&s_row[w][8 * j + 4 * hl]);
-        srow[4 * j + 0] = q4.x;
-        srow[4 * j + 1] = q4.y;
-        srow[4 * j + 2] = q4.z;
-        srow[4 * j + 3] = q4.w;
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int n = 0; n < NC; ++n) {
-        v16i acc = {};
-        if constexpr (G == 32) {
-          const v4i vb = *reinterpret_cast<const v4i*>(&s_v[2 * g + hl][32 * n + rl][0]);
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(wq[g], vb, acc, 0, 0, 0);
-        } else {
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-            const v4i vb = *reinterpret_cast<const v4i*>(&s_v[2 * kh + hl][32 * n + rl][0]);
-            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(wq[kh], vb, acc, 0, 0, 0);
-          }
+          for (int i = 0; i < 4; ++i) O[n][i] += swg[g] * (float)c[i];
         }
+      }
+    } else {
+      const long wb0 = (long)(((uint64_t)wpk[0][1] << 32) | wpk[0][0]);
+      const long wb1 = (long)(((uint64_t)wpk[1][1] << 32) | wpk[1][0]);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) O[n][v] += srow[v] * (float)acc[v];
+      for (int n = 0; n < NN; ++n) {
+        const long va0 = *reinterpret_cast<const long*>(&s_v[lg >> 1][16 * n + lr][vpage_off]);
+        const long va1 = *reinterpret_cast<const long*>(&s_v[2 + (lg >> 1)][16 * n + lr][vpage_off]);
+        v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(va0, wb0, v4i{0, 0, 0, 0}, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_i32_16x16x32_i8(va1, wb1, c, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[n][i] += swg[0] * (float)c[i];
       }
     }
   }
 
-  // ---- O / l and store --------------------------------------------------------
-  const float l_row = lpart + __shfl_xor(lpart, 32, kWave);
-  if (hl == 0) s_row[w][rl] = l_row;
-  wave_lds_sync();
-  float lrow[16];
+  // ---- O / l and store: lane l holds row l%16, dims 16n + 4(l/16) + i ----------
+  const float l_row = row_sum4(lsum);
+  if (!row_ok) return;
+  const float inv = 1.0f / l_row;
+  float* dst = a.out + qrow * D + 4 * lg;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float4 q4 = *reinterpret_cast<const float4*>(&s_row[w][8 * j + 4 * hl]);
-    lrow[4 * j + 0] = q4.x;
-    lrow[4 * j + 1] = q4.y;
-    lrow[4 * j + 2] = q4.z;
-    lrow[4 * j + 3] = q4.w;
-  }
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int r = 8 * (v / 4) + 4 * hl + (v % 4);
-    const int fr2 = row0 + 32 * w + r;
-    if (fr2 >= nrows_seq) continue;
-    const int tk = fr2 / grp, hd = fr2 % grp;
-    float* dst = a.out + ((size_t)(q0 + tk) * a.num_q_heads + (size_t)kv * grp + hd) * D;
-    const float inv = 1.0f / lrow[v];
-#pragma unroll
-    for (int n = 0; n < NC; ++n) dst[32 * n + rl] = O[n][v] * inv;
-  }
+  for (int n = 0; n < NN; ++n)
+    *reinterpret_cast<float4*>(dst + 16 * n) =
+        make_float4(O[n][0] * inv, O[n][1] * inv, O[n][2] * inv, O[n][3] * inv);
 }
 
 hipError_t launch_prefix_prefill(const PrefillArgs& a, hipStream_t stream) {
