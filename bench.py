@@ -49,6 +49,13 @@ def parse_args():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--prefill-reps", type=int, default=10)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--sweep", action="store_true",
+                   help="also time every decode configuration and prefill at G=32/64")
+    p.add_argument("--no-graph", action="store_true",
+                   help="launch eagerly instead of replaying HIP graphs (for counter runs)")
+    p.add_argument("--copy-calibration-mb", type=float, default=0.0,
+                   help="only run a plain device copy of this size (for scaling HBM "
+                        "byte counters) and exit")
     return p.parse_args()
 
 
@@ -129,18 +136,20 @@ def time_decode(args, log_prefix=""):
     torch.cuda.synchronize()
 
     def capture(fn, n):
+        if args.no_graph:
+            return lambda: [fn(i) for i in range(n)]
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(n):
                 fn(i)
-        return g
+        return g.replay
 
     def replay_ms(g):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
-        g.replay()
+        g()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
@@ -159,7 +168,7 @@ def time_decode(args, log_prefix=""):
                 decode_us=1e3 * float(np.median(dec_ms)), decode_us_runs=[1e3 * x for x in dec_ms])
 
 
-def time_prefill(reps, G=32):
+def time_prefill(reps, G=32, graph=True):
     import numpy as np
     import torch
 
@@ -185,14 +194,18 @@ def time_prefill(reps, G=32):
     for _ in range(2):
         run()
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(reps):
-            run()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                run()
+        replay = g.replay
+    else:
+        replay = lambda: [run() for _ in range(reps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    g.replay()
+    replay()
     e1.record()
     torch.cuda.synchronize()
     us = 1e3 * e0.elapsed_time(e1) / reps
@@ -225,8 +238,25 @@ def cpu_baseline(wl, G, seconds):
                        f"host has {os.cpu_count()} logical CPUs)")
 
 
+def copy_calibration(mb, reps=10):
+    """A plain device-to-device copy of known size: its FETCH_SIZE/WRITE_SIZE
+    counters give the scale factor for the kernels' byte counters."""
+    import torch
+    n = int(mb * 1e6) // 16 * 16
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": reps}), flush=True)
+
+
 def main():
     args = parse_args()
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU component).", file=sys.stderr)
@@ -249,12 +279,33 @@ def main():
                  producer_us=round(r["producer_us"], 3), effective_kv_bytes=eff,
                  cache_copies_rotated=r["copies"])
     if not args.no_prefill:
-        pf = time_prefill(args.prefill_reps)
+        pf = time_prefill(args.prefill_reps, graph=not args.no_graph)
         log(f"prefill {pf['workload']}: {pf['us']:.1f} us, {pf['tops']:.1f} int8 TOPS "
             f"({100 * pf['tops'] / INT8_PEAK_TOPS:.1f}% of peak)")
         extra.update(prefill_us=round(pf["us"], 2), prefill_int8_tops=round(pf["tops"], 2),
                      prefill_frac_of_int8_peak=round(pf["tops"] / INT8_PEAK_TOPS, 4),
                      prefill_ops=pf["ops"])
+    if args.sweep:
+        sweep = {}
+        for name in ["decode_L512", "decode_L4096", "decode_L8192", "decode_L16384",
+                     "decode_L32768", "decode_batch16", "mha_producer_decode"]:
+            for G in (32, 64):
+                a2 = argparse.Namespace(**vars(args))
+                a2.workload, a2.w_group, a2.steps, a2.warmup = name, G, 50, 5
+                rr = time_decode(a2, log_prefix="  sweep ")
+                b = rr["wl"].effective_kv_bytes()
+                sweep[f"{name}_G{G}"] = dict(
+                    decode_us=round(rr["decode_us"], 3), producer_us=round(rr["producer_us"], 3),
+                    step_us=round(rr["ms_per_step"] * 1e3, 3),
+                    decode_gbs=round(b / (rr["decode_us"] * 1e-6) / 1e9, 1),
+                    decode_frac_hbm=round(b / (rr["decode_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+                log(f"  sweep {name} G={G}: {sweep[f'{name}_G{G}']}")
+        for G in (32, 64):
+            pf = time_prefill(args.prefill_reps, G, graph=not args.no_graph)
+            sweep[f"prefill_G{G}"] = dict(us=round(pf["us"], 2), tops=round(pf["tops"], 2),
+                                          frac_int8=round(pf["tops"] / INT8_PEAK_TOPS, 4))
+            log(f"  sweep prefill G={G}: {sweep[f'prefill_G{G}']}")
+        extra["sweep"] = sweep
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.w_group, args.cpu_seconds)

@@ -15,7 +15,7 @@
 //
 // gfx950 mapping.  A workgroup of 12 waves owns 192 consecutive flattened
 // rows (query token, q head of the GQA group) of one (sequence, KV head) --
-// 32 tokens x 6 heads for Qwen-like 24/4 heads; wave w owns 16 rows and lane
+// 32 tokens x 6 heads for 24 q heads over 4 KV heads; wave w owns 16 rows and lane
 // l row l%16 (the four lanes l%16 + 16j share a row).  K/V tiles of 64 keys
 // are staged in LDS in their page layouts.
 //  * QK, transposed: S^T = K Q^T with v_mfma_i32_16x16x64_i8 (operand A = 16
@@ -33,6 +33,8 @@
 //    the output is rescaled only when the running max grows by more than 8
 //    (p~ stays below 2^8), which is exact in real arithmetic since Wq and O
 //    do not depend on the reference max.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -64,17 +66,38 @@ __device__ __forceinline__ float row_sum4(float v) {
 
 }  // namespace
 
+// K tile row of one key: D bytes plus 16 of padding, and every 16-key block
+// shifted by 64 bytes more than the previous one.  With this layout the 16
+// keys one QK operand read touches (keys 8(r/4) + 4b + r%4 of a 32-key
+// group) hit 16 distinct 4-bank groups of the 64 LDS banks for D = 64, 128
+// and 256, and no two key rows overlap.
+template <int D>
+__device__ __forceinline__ int k_lds_off(int key) {
+  return key * (D + 16) + ((key >> 4) << 6);
+}
+
+template <int D>
+struct PrefillTile {
+  static constexpr int kBytes = kKT * (D + 16) + (kKT / 16 - 1) * 64;  // K tile (padded)
+  static constexpr int vBytes = kKT / 16 * D * 16;    // V tile [page][dim][16]
+  static constexpr int kUnits = kKT / 16 * D;         // 16-byte units per operand
+};
+
 template <int D, int G>
 __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs a) {
   constexpr int NC = D / 64;   // 64-dim k-steps of QK
   constexpr int NN = D / 16;   // 16-dim output tiles of PV
   constexpr int NT = kNW * kWave;
-  // LDS tiles in page layout: K [page][chunk][key][16 B], V [page][dim][16 B]
-  __shared__ __attribute__((aligned(16))) int8_t s_k[kKT / 16][D / 16][16][16];
-  __shared__ __attribute__((aligned(16))) int8_t s_v[kKT / 16][D][16];
-  __shared__ __attribute__((aligned(16))) float s_sk[kKT];
-  __shared__ __attribute__((aligned(16))) float s_sv[kKT];
-  __shared__ int s_pid[kKT / 16];
+  constexpr int KB = PrefillTile<D>::kBytes, VB = PrefillTile<D>::vBytes;
+  constexpr int UNITS = PrefillTile<D>::kUnits;
+  constexpr int UPT = (2 * UNITS + NT - 1) / NT;  // 16-byte units per thread per tile
+  constexpr int kMaxBt = 4096;                    // block-table entries kept in LDS
+
+  __shared__ __attribute__((aligned(16))) int8_t s_k[2][KB];
+  __shared__ __attribute__((aligned(16))) int8_t s_v[2][VB];
+  __shared__ __attribute__((aligned(16))) float s_sk[2][kKT];
+  __shared__ __attribute__((aligned(16))) float s_sv[2][kKT];
+  __shared__ int s_bt[kMaxBt];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lg = lane >> 4, lr = lane & 15;
@@ -102,8 +125,10 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
   for (int c = 0; c < NC; ++c)
     qb[c] = row_ok ? *reinterpret_cast<const v4i*>(a.q_int8 + qrow * D + 64 * c + 16 * lg)
                    : v4i{0, 0, 0, 0};
-  // score in log2 units: s2 = acc * sK * (sQ * softmax_scale * log2 e)
-  const float crow = row_ok ? a.q_scale[qrow] * a.softmax_scale * kLog2e : 0.0f;
+  // score in log2 units: s2 = acc * sK * (sQ * softmax_scale * log2 e).  A row
+  // past the chunk gets crow = 1 and mref = +inf, which makes all its p~ zero
+  // without a select (its queries are zero, so its scores are 0 or -inf).
+  const float crow = row_ok ? a.q_scale[qrow] * a.softmax_scale * kLog2e : 1.0f;
 
   const int last_fr = min(row0 + kRows, nrows_seq) - 1;
   const int nkeys = ctx + last_fr / grp + 1;  // keys visible to the workgroup's last row
@@ -114,60 +139,83 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
   const int wave_min_pos = wave_live ? ctx + wave_first_fr / grp : 0;
   const int ntiles = (nkeys + kKT - 1) / kKT;
   const int npages_seq = min((seq_len + kBlockSize - 1) / kBlockSize, a.max_blocks_per_seq);
+  const int npages_used = min((nkeys + kBlockSize - 1) / kBlockSize, npages_seq);
+  const bool bt_in_lds = npages_used <= kMaxBt;
+  const int32_t* bt_row = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  if (bt_in_lds)
+    for (int i = tid; i < npages_used; i += NT)
+      s_bt[i] = min(max(bt_row[i], 0), a.num_blocks - 1);
+  __syncthreads();
+  auto page_id = [&](int pg) -> int {
+    if (pg >= npages_used) return -1;
+    return bt_in_lds ? s_bt[pg] : min(max(bt_row[pg], 0), a.num_blocks - 1);
+  };
 
-  float mref = -INFINITY;  // reference max (log2 units) of this row
-  float lsum = 0.0f;       // this lane's share of l
+  // ---- tile staging: global -> registers (next tile) -> LDS ------------------
+  v4i stg[UPT];
+  float stg_sk = 0.0f, stg_sv = 0.0f;
+  auto load_tile = [&](int t) {
+    const int k0 = t * kKT;
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+      const int u = tid + j * NT;
+      stg[j] = v4i{0, 0, 0, 0};
+      if (u < 2 * UNITS) {
+        const int isv = u >= UNITS;
+        const int uu = isv ? u - UNITS : u;
+        const int pid = page_id(k0 / kBlockSize + uu / D);
+        if (pid >= 0)
+          stg[j] = *reinterpret_cast<const v4i*>((isv ? a.v_cache : a.k_cache) +
+                                                 ((size_t)pid * Hkv + kv) * (size_t)D * 16 +
+                                                 (size_t)(uu % D) * 16);
+      }
+    }
+    if (tid < kKT) {
+      const int key = k0 + tid;
+      const int pid = page_id(key / kBlockSize);
+      stg_sk = stg_sv = 0.0f;
+      if (pid >= 0 && key < seq_len) {
+        const size_t idx = ((size_t)pid * kBlockSize + (tid % 16)) * Hkv + kv;
+        stg_sk = a.k_scale[idx];
+        stg_sv = a.v_scale[idx];
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+      const int u = tid + j * NT;
+      if (u < 2 * UNITS) {
+        if (u >= UNITS) {
+          const int uu = u - UNITS;  // V: page uu / D, dim uu % D
+          *reinterpret_cast<v4i*>(&s_v[buf][uu * 16]) = stg[j];
+        } else {  // K: page u / D, chunk (u % D) / 16, key in page u % 16
+          const int key = 16 * (u / D) + (u % 16);
+          *reinterpret_cast<v4i*>(&s_k[buf][k_lds_off<D>(key) + 16 * ((u % D) / 16)]) = stg[j];
+        }
+      }
+    }
+    if (tid < kKT) {
+      s_sk[buf][tid] = stg_sk;
+      s_sv[buf][tid] = stg_sv;
+    }
+  };
+
+  float mref = row_ok ? -INFINITY : INFINITY;  // reference max (log2 units)
+  float lsum = 0.0f;                           // this lane's share of l
   float O[NN][4];
 #pragma unroll
   for (int n = 0; n < NN; ++n)
 #pragma unroll
     for (int i = 0; i < 4; ++i) O[n][i] = 0.0f;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * kKT;
-    __syncthreads();
-    if (tid < kKT / 16) {
-      const int pg = k0 / kBlockSize + tid;
-      int pid = -1;
-      if (pg < npages_seq) {
-        pid = a.block_tables[(size_t)s * a.max_blocks_per_seq + pg];
-        pid = min(max(pid, 0), a.num_blocks - 1);
-      }
-      s_pid[tid] = pid;
-    }
-    __syncthreads();
-    // K and V pages of the tile: 4 x (D*16) bytes each, 16 bytes per thread-step
-    constexpr int kUnits = kKT / 16 * D;  // 16-byte units per tile and operand
-    for (int u = tid; u < 2 * kUnits; u += NT) {
-      const int isv = u >= kUnits;
-      const int uu = isv ? u - kUnits : u;
-      const int i = uu / D, rem = uu % D;
-      const int pid = s_pid[i];
-      v4i val = {0, 0, 0, 0};
-      const int8_t* src = (isv ? a.v_cache : a.k_cache) + ((size_t)pid * Hkv + kv) * (size_t)D * 16 +
-                          (size_t)rem * 16;
-      if (pid >= 0) val = *reinterpret_cast<const v4i*>(src);
-      int8_t* dst = isv ? &s_v[i][rem][0] : &s_k[i][rem / 16][rem % 16][0];
-      *reinterpret_cast<v4i*>(dst) = val;
-    }
-    if (tid < kKT) {
-      const int key = k0 + tid;
-      const int pid = s_pid[tid / 16];
-      float skv = 0.0f, svv = 0.0f;
-      if (pid >= 0 && key < seq_len) {
-        const size_t idx = ((size_t)pid * kBlockSize + (tid % 16)) * Hkv + kv;
-        skv = a.k_scale[idx];
-        svv = a.v_scale[idx];
-      }
-      s_sk[tid] = skv;
-      s_sv[tid] = svv;
-    }
-    __syncthreads();
-    if (k0 >= wave_nkeys) continue;  // no key of this tile is visible to the wave
-    const bool diag = k0 + kKT - 1 > wave_min_pos;  // some key may be masked
-
-    // ---- S^T = K Q^T: per 32-key group g, two chains of D/64 MFMAs ---------
-    float u2[2][8];  // [group][key 8lg + j]: acc * sK, -inf when masked
+  // One 64-key tile from LDS buffer `buf`; MASK: keys past a row's position
+  // may be present (diagonal tiles only).
+  auto compute_tile = [&](int buf, int k0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int8_t* kt = s_k[buf];
+    // ---- S^T = K Q^T: per 32-key group g, two chains of D/64 MFMAs -------
+    float u2[2][8];
     float mt = -INFINITY;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -176,58 +224,49 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
       for (int b = 0; b < 2; ++b) {
         acc[b] = v4i{0, 0, 0, 0};
         const int krow = 32 * g + 8 * (lr >> 2) + 4 * b + (lr & 3);  // key of A row lr
+        const int8_t* kp = kt + k_lds_off<D>(krow) + 16 * lg;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const v4i ka =
-              *reinterpret_cast<const v4i*>(&s_k[krow >> 4][4 * c + lg][krow & 15][0]);
+          const v4i ka = *reinterpret_cast<const v4i*>(kp + 64 * c);
           acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qb[c], acc[b], 0, 0, 0);
         }
       }
-      const float4 sk0 = *reinterpret_cast<const float4*>(&s_sk[32 * g + 8 * lg]);
-      const float4 sk1 = *reinterpret_cast<const float4*>(&s_sk[32 * g + 8 * lg + 4]);
+      const float4 sk0 = *reinterpret_cast<const float4*>(&s_sk[buf][32 * g + 8 * lg]);
+      const float4 sk1 = *reinterpret_cast<const float4*>(&s_sk[buf][32 * g + 8 * lg + 4]);
       const float skv[8] = {sk0.x, sk0.y, sk0.z, sk0.w, sk1.x, sk1.y, sk1.z, sk1.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float x = (float)acc[j >> 2][j & 3] * skv[j];
-        if (diag) {
-          const int key = k0 + 32 * g + 8 * lg + j;
-          x = (row_ok && key <= pos) ? x : -INFINITY;
-        }
+        if constexpr (MASK) x = (k0 + 32 * g + 8 * lg + j <= pos) ? x : -INFINITY;
         u2[g][j] = x;
         mt = fmaxf(mt, x);
       }
     }
-    // ---- online softmax (base 2, lazy rescale) -----------------------------
-    mt = row_max4(mt) * crow;  // crow > 0: max of the scaled scores
-    if (!row_ok) mt = -INFINITY;
-    const bool grow = mt > mref + kLazy || mref == -INFINITY;
-    if (__builtin_amdgcn_ballot_w64(grow && mt != -INFINITY)) {
-      const float mnew = (grow && mt != -INFINITY) ? mt : mref;
-      const float alpha = (mref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mref - mnew);
-      if (mnew != mref) {
-        lsum *= alpha;
+    // ---- online softmax (base 2, lazy rescale) -------------------------------
+    mt = row_max4(mt) * crow;
+    const bool grow = row_ok && mt != -INFINITY && (mt > mref + kLazy || mref == -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? (mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mref - mt))
+                               : 1.0f;
+      if (grow) mref = mt;
+      lsum *= alpha;
 #pragma unroll
-        for (int n = 0; n < NN; ++n)
+      for (int n = 0; n < NN; ++n)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) O[n][i] *= alpha;
-        mref = mnew;
-      }
+        for (int i = 0; i < 4; ++i) O[n][i] *= alpha;
     }
     // p~ = 2^(s2 - mref), W = p~ sV, Wq = round(W * 127 / max W)
     uint32_t wpk[2][2];
-    float swg[2];
-    float am[2];
-    float Wv[2][8];
+    float swg[2], am[2], Wv[2][8];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const float4 sv0 = *reinterpret_cast<const float4*>(&s_sv[32 * g + 8 * lg]);
-      const float4 sv1 = *reinterpret_cast<const float4*>(&s_sv[32 * g + 8 * lg + 4]);
+      const float4 sv0 = *reinterpret_cast<const float4*>(&s_sv[buf][32 * g + 8 * lg]);
+      const float4 sv1 = *reinterpret_cast<const float4*>(&s_sv[buf][32 * g + 8 * lg + 4]);
       const float svv[8] = {sv0.x, sv0.y, sv0.z, sv0.w, sv1.x, sv1.y, sv1.z, sv1.w};
       float mx = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pt =
-            row_ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(u2[g][j], crow, -mref)) : 0.0f;
+        const float pt = __builtin_amdgcn_exp2f(__builtin_fmaf(u2[g][j], crow, -mref));
         lsum += pt;
         Wv[g][j] = pt * svv[j];
         mx = fmaxf(mx, Wv[g][j]);
@@ -238,26 +277,27 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       swg[g] = am[g] * (1.0f / 127.0f);
+      // 127 / max W; W * inv + 0.5 stays below 128 since W <= max W and the
+      // reciprocal is within an ulp, so truncation gives round-half-up in [0, 127]
       const float inv = am[g] > 0.0f ? 127.0f * __builtin_amdgcn_rcpf(am[g]) : 0.0f;
       uint32_t pk[2] = {0, 0};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t q = min((uint32_t)__builtin_fmaf(Wv[g][j], inv, 0.5f), 127u);
-        pk[j >> 2] |= q << (8 * (j & 3));
-      }
+      for (int j = 0; j < 8; ++j)
+        pk[j >> 2] |= (uint32_t)__builtin_fmaf(Wv[g][j], inv, 0.5f) << (8 * (j & 3));
       wpk[g][0] = pk[0];
       wpk[g][1] = pk[1];
     }
-    // ---- O^T += sW * (V^T Wq^T) ------------------------------------------------
-    const int vpage_off = 8 * (lg & 1);
+    // ---- O^T += sW * (V^T Wq^T) --------------------------------------------------
+    const int8_t* vt = s_v[buf];
+    const int voff = 8 * (lg & 1);
     if constexpr (G == 32) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const long wb = (long)(((uint64_t)wpk[g][1] << 32) | wpk[g][0]);
-        const int vpg = 2 * g + (lg >> 1);
+        const int8_t* vp = vt + ((2 * g + (lg >> 1)) * D + lr) * 16 + voff;
 #pragma unroll
         for (int n = 0; n < NN; ++n) {
-          const long va = *reinterpret_cast<const long*>(&s_v[vpg][16 * n + lr][vpage_off]);
+          const long va = *reinterpret_cast<const long*>(vp + 256 * n);
           const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(va, wb, v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) O[n][i] += swg[g] * (float)c[i];
@@ -266,16 +306,33 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
     } else {
       const long wb0 = (long)(((uint64_t)wpk[0][1] << 32) | wpk[0][0]);
       const long wb1 = (long)(((uint64_t)wpk[1][1] << 32) | wpk[1][0]);
+      const int8_t* vp0 = vt + ((lg >> 1) * D + lr) * 16 + voff;
+      const int8_t* vp1 = vt + ((2 + (lg >> 1)) * D + lr) * 16 + voff;
 #pragma unroll
       for (int n = 0; n < NN; ++n) {
-        const long va0 = *reinterpret_cast<const long*>(&s_v[lg >> 1][16 * n + lr][vpage_off]);
-        const long va1 = *reinterpret_cast<const long*>(&s_v[2 + (lg >> 1)][16 * n + lr][vpage_off]);
+        const long va0 = *reinterpret_cast<const long*>(vp0 + 256 * n);
+        const long va1 = *reinterpret_cast<const long*>(vp1 + 256 * n);
         v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(va0, wb0, v4i{0, 0, 0, 0}, 0, 0, 0);
         c = __builtin_amdgcn_mfma_i32_16x16x32_i8(va1, wb1, c, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[n][i] += swg[0] * (float)c[i];
       }
     }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int k0 = t * kKT;
+    if (t + 1 < ntiles) load_tile(t + 1);  // in flight during this tile's compute
+    if (k0 < wave_nkeys) {
+      if (k0 + kKT - 1 > wave_min_pos) compute_tile(buf, k0, std::true_type{});
+      else compute_tile(buf, k0, std::false_type{});
+    }
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
   }
 
   // ---- O / l and store: lane l holds row l%16, dims 16n + 4(l/16) + i ----------
