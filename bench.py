@@ -300,7 +300,7 @@ def main():
                     decode_gbs=round(b / (rr["decode_us"] * 1e-6) / 1e9, 1),
                     decode_frac_hbm=round(b / (rr["decode_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
                 log(f"  sweep {name} G={G}: {sweep[f'{name}_G{G}']}")
-        for G in (32, 64):
+        for G in ((32, 64) if not args.no_prefill else ()):
             pf = time_prefill(args.prefill_reps, G, graph=not args.no_graph)
             sweep[f"prefill_G{G}"] = dict(us=round(pf["us"], 2), tops=round(pf["tops"], 2),
                                           frac_int8=round(pf["tops"] / INT8_PEAK_TOPS, 4))

@@ -36,8 +36,9 @@
 //      Wave w owns output dims [w D/8, (w+1) D/8).
 //    A single-partition sequence writes the output; otherwise (m_p, l_p, o_p)
 //    go to the workspace.
-// 2. paged_decode_merge_kernel: one workgroup per (sequence, q head) merges
-//    its partitions, O = sum w_p o_p / sum w_p with w_p = l_p exp(m_p - M).
+// 2. paged_decode_merge_kernel: one wave per (q head, sequence, 64 output
+//    dims) merges the partitions, O = sum w_p o_p / sum w_p with
+//    w_p = l_p exp(m_p - M).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -96,8 +97,44 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   const int grp = a.group;
   const int Hkv = a.num_kv_heads;
 
-  int L = a.seq_lens[s];
-  L = min(max(L, 0), a.max_seq_len);
+  // ---- first round trip: the sequence length, the block-table entries of the
+  // pages this thread reads, the queries and their scales.  None of them
+  // depends on another, so they are all in flight together.
+  const int L_raw = a.seq_lens[s];
+  const int32_t* bt_row = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  auto bt_at = [&](int j) { return bt_row[min(p * 16 + j, a.max_blocks_per_seq - 1)]; };
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int tsv = tid & (kPartition - 1);  // V scale of token tsv (threads >= 256 repeat)
+  int pidk[PPW], pidv[4];
+#pragma unroll
+  for (int j = 0; j < PPW; ++j) pidk[j] = bt_at(wu * PPW + j);  // K pages of this wave
+#pragma unroll
+  for (int g = 0; g < 4; ++g) pidv[g] = bt_at(4 * g + lg);      // V pages of this lane
+  int pids = bt_at(tsv >> 4);
+  v4i qa[NC];
+  {
+    const bool vh = lr < grp;
+    const int8_t* qp = a.q_int8 +
+                       ((size_t)s * a.num_q_heads + (size_t)kv * grp + (vh ? lr : 0)) * D + 16 * lg;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qa[c] = *reinterpret_cast<const v4i*>(qp + 64 * c);
+      if (!vh) qa[c] = v4i{0, 0, 0, 0};
+    }
+  }
+  float sq[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * lg + r;
+    sq[r] = a.q_scale[(size_t)s * a.num_q_heads + (size_t)kv * grp + min(h, grp - 1)];
+    if (h >= grp) sq[r] = 0.0f;
+  }
+
+  // keep the loads above ahead of the early exits below (the compiler would
+  // otherwise sink them past the wait for the sequence length)
+  asm volatile("" ::: "memory");
+
+  const int L = min(max(L_raw, 0), a.max_seq_len);
   const int P_s = (L + kPartition - 1) / kPartition;
   float* out_base = a.out + ((size_t)s * a.num_q_heads + (size_t)kv * grp) * D;
   if (L == 0) {
@@ -107,56 +144,46 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   }
   if (p >= P_s) return;
   const int tok0 = p * kPartition;
-  const int npages = min(16, (L + kBlockSize - 1) / kBlockSize - p * 16);
+  // Entries past the sequence are clamped to a valid page: what they load is
+  // discarded (scores of tokens >= L are -inf and their W and scales are 0).
+  auto clamp_page = [&](int pg) { return min(max(pg, 0), a.num_blocks - 1); };
+#pragma unroll
+  for (int j = 0; j < PPW; ++j) pidk[j] = clamp_page(pidk[j]);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) pidv[g] = clamp_page(pidv[g]);
+  pids = clamp_page(pids);
 
-  // ---- page ids: lane j < 16 of every wave holds page j ----------------------
-  int my_pid = 0;
-  if (lane < npages) {
-    my_pid = a.block_tables[(size_t)s * a.max_blocks_per_seq + p * 16 + lane];
-    my_pid = min(max(my_pid, 0), a.num_blocks - 1);
-  }
-
-  // ---- issue every load of the partition -----------------------------------
-  v4i kb[PPW][NC];
-  int pidw[PPW];
-#pragma unroll
-  for (int j = 0; j < PPW; ++j) {
-    const int pi = w * PPW + j;
-    pidw[j] = __shfl(my_pid, pi, kWave);
-    const int8_t* base = a.k_cache + ((size_t)pidw[j] * Hkv + kv) * (size_t)(D / 16) * 256;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      kb[j][c] = (pi < npages) ? *reinterpret_cast<const v4i*>(base + (4 * c + lg) * 256 + lr * 16)
-                               : v4i{0, 0, 0, 0};
-  }
-  v4i qa[NC];
-  {
-    const bool vh = lr < grp;
-    const int8_t* qp = a.q_int8 +
-                       ((size_t)s * a.num_q_heads + (size_t)kv * grp + (vh ? lr : 0)) * D + 16 * lg;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qa[c] = vh ? *reinterpret_cast<const v4i*>(qp + 64 * c) : v4i{0, 0, 0, 0};
-  }
+  // ---- second round trip: every scale, K and V byte of the partition, issued
+  // in the order they are consumed (scales, K, V) so each wait is partial ----
   float sk[PPW];
 #pragma unroll
-  for (int j = 0; j < PPW; ++j) {
-    const int tok = tok0 + 16 * (w * PPW + j) + lr;
-    sk[j] = tok < L ? a.k_scale[((size_t)pidw[j] * kBlockSize + lr) * Hkv + kv] : 0.0f;
-  }
-  float sq[4];
+  for (int j = 0; j < PPW; ++j) sk[j] = a.k_scale[((size_t)pidk[j] * kBlockSize + lr) * Hkv + kv];
+  const float sv_ld = a.v_scale[((size_t)pids * kBlockSize + (tsv & 15)) * Hkv + kv];
+  __builtin_amdgcn_sched_barrier(0);
+  v4i kb[PPW][NC];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * lg + r;
-    sq[r] = h < grp ? a.q_scale[(size_t)s * a.num_q_heads + (size_t)kv * grp + h] : 0.0f;
+  for (int j = 0; j < PPW; ++j) {
+    const int8_t* base = a.k_cache + ((size_t)pidk[j] * Hkv + kv) * (size_t)(D / 16) * 256;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      kb[j][c] = *reinterpret_cast<const v4i*>(base + (4 * c + lg) * 256 + lr * 16);
   }
-  // V scales of the partition to LDS (thread t < 256: token t)
-  for (int t = tid; t < kPartition; t += NT) {
-    const int pid = __shfl(my_pid, (t >> 4) & 15, kWave);
-    s_sv[t] = (tok0 + t < L) ? a.v_scale[((size_t)pid * kBlockSize + (t & 15)) * Hkv + kv] : 0.0f;
+  __builtin_amdgcn_sched_barrier(0);
+  v4i vb[4][NCW];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int8_t* base = a.v_cache + ((size_t)pidv[g] * Hkv + kv) * (size_t)D * 16;
+#pragma unroll
+    for (int c = 0; c < NCW; ++c)
+      vb[g][c] = *reinterpret_cast<const v4i*>(base + (DecodeShape<D>::DW * w + 16 * c + lr) * 16);
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < PPW; ++j)
+    if (tok0 + 16 * (w * PPW + j) + lr >= L) sk[j] = 0.0f;
+  if (tid < kPartition) s_sv[tid] = (tok0 + tid < L) ? sv_ld : 0.0f;
 
-  // ---- QK (K arrives first), then the V loads, then scores -> LDS ------------
+  // ---- QK, then scores -> LDS ----------------------------------------------
   v4i qk[PPW];
 #pragma unroll
   for (int j = 0; j < PPW; ++j) {
@@ -165,22 +192,6 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
     for (int c = 0; c < NC; ++c)
       qk[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[c], kb[j][c], qk[j], 0, 0, 0);
   }
-  // V is requested only once this wave's K has arrived, so K is not queued
-  // behind V and the softmax below overlaps the V transfer.
-  __builtin_amdgcn_sched_barrier(0);
-  v4i vb[4][NCW];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int pi = 4 * g + lg;
-    const int pid = __shfl(my_pid, pi, kWave);
-    const int8_t* base = a.v_cache + ((size_t)pid * Hkv + kv) * (size_t)D * 16;
-#pragma unroll
-    for (int c = 0; c < NCW; ++c)
-      vb[g][c] = (pi < npages)
-                     ? *reinterpret_cast<const v4i*>(base + (DecodeShape<D>::DW * w + 16 * c + lr) * 16)
-                     : v4i{0, 0, 0, 0};
-  }
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < PPW; ++j) {
     const int tl = 16 * (w * PPW + j) + lr;
@@ -299,104 +310,78 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   }
 }
 
-// One workgroup of 256 threads per (sequence, q head, 64-dim slice):
+// One wave per (q head, sequence, 64-dim slice), no barriers:
 //   O = sum_p w_p o_p / sum_p w_p, w_p = l_p exp(m_p - M), M = max_p m_p.
-// Thread t owns float4 column t % 16 of the slice for partitions
-// p = t / 16 (mod 16).  The partial loads of a round do not depend on the
-// weights, so they are in flight while (m_p, l_p) are read and the weights
-// computed; the 16 row groups are summed in LDS at the end.
+// Lane l owns float4 column l % 16 of the slice for partitions p = l / 16
+// (mod 4), U per round; the partial loads of the first round and lane l's
+// (m_l, l_l) go out before the sequence length is known (every slot below
+// max_parts exists in the workspace; slots past the sequence are discarded).
+// The weight of partition p is computed by lane p % 64 and fetched with a
+// cross-lane read; the four lane groups are summed with two swaps.
 template <int D>
-__global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeArgs a) {
-  constexpr int NCOL = 16;         // float4 columns of a 64-dim slice
-  constexpr int NR = 256 / NCOL;   // row groups
-  constexpr int U = 4;             // partitions per thread per round
-  constexpr int RP = NR * U;       // partitions per round
-  constexpr int kMaxParts = 4096;  // max_seq_len <= 2^20
-  __shared__ float s_w[kMaxParts];
-  __shared__ float s_red[4];
-  __shared__ __attribute__((aligned(16))) float4 s_acc[NR][NCOL];
-  const int h = blockIdx.x, s = blockIdx.y, slice = blockIdx.z, tid = threadIdx.x;
+__global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a) {
+  constexpr int U = 16;            // partitions per lane per round
+  constexpr int RP = 4 * U;        // partitions per round (= 64)
+  const int h = blockIdx.x, s = blockIdx.y, slice = blockIdx.z, lane = threadIdx.x;
   const int grp = a.group;
   const int kv = h / grp, hh = h % grp;
   const size_t base = ((size_t)s * a.num_kv_heads + kv) * a.max_parts;
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + base * grp + hh;
-  const int col = tid % NCOL, rg = tid / NCOL;
+  const int col = lane & 15, lg = lane >> 4;
   const size_t ostride = (size_t)grp * D;
   const float* po = a.part_o + (base * grp + hh) * D + 64 * slice + 4 * col;
-  // The first round of partial loads and this thread's (m, l) are requested
-  // before the sequence length arrives (all slots below max_parts exist in
-  // the workspace; slots past the sequence are discarded by selects).
   float4 v[U];
   auto issue = [&](int q0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int q = min(q0 + rg + u * NR, a.max_parts - 1);
+      const int q = min(q0 + lg + 4 * u, a.max_parts - 1);
       v[u] = *reinterpret_cast<const float4*>(po + (size_t)q * ostride);
     }
   };
   issue(0);
-  const float2 ml0 = ml[(size_t)min(tid, a.max_parts - 1) * grp];
+  const float2 ml0 = ml[(size_t)min(lane, a.max_parts - 1) * grp];
   int L = a.seq_lens[s];
   L = min(max(L, 0), a.max_seq_len);
   const int P_s = (L + kPartition - 1) / kPartition;
   if (P_s <= 1) return;  // written by the partition kernel
 
-  float m = tid < P_s ? ml0.x : -INFINITY;
-  for (int q = tid + 256; q < P_s; q += 256) m = fmaxf(m, ml[(size_t)q * grp].x);
-  m = group_max<kWave>(m);
-  if ((tid & 63) == 0) s_red[tid >> 6] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  float wpart = 0.0f;
-  if (tid < P_s) {
-    const float wq = ml0.y * expf(ml0.x - M);
-    s_w[tid] = wq;
-    wpart = wq;
-  }
-  for (int q = tid + 256; q < P_s; q += 256) {
-    const float2 e = ml[(size_t)q * grp];
-    const float wq = e.y * expf(e.x - M);
-    s_w[q] = wq;
-    wpart += wq;
-  }
-  wpart = group_sumf<kWave>(wpart);
-  __syncthreads();
-  if ((tid & 63) == 0) s_red[tid >> 6] = wpart;
-  __syncthreads();
-  const float wsum = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+  float m = lane < P_s ? ml0.x : -INFINITY;
+  for (int q = lane + RP; q < P_s; q += RP) m = fmaxf(m, ml[(size_t)q * grp].x);
+  const float M = group_max<kWave>(m);
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wsum = 0.0f;
   for (int q0 = 0; q0 < P_s; q0 += RP) {
+    float wl = 0.0f;  // weight of partition q0 + lane
+    if (q0 + lane < P_s) {
+      const float2 e = q0 == 0 ? ml0 : ml[(size_t)(q0 + lane) * grp];
+      wl = e.y * expf(e.x - M);
+    }
+    wsum += wl;
     if (q0 > 0) issue(q0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int q = q0 + rg + u * NR;
-      if (q < P_s) {
-        const float wq = s_w[q];
-        acc.x += wq * v[u].x;
-        acc.y += wq * v[u].y;
-        acc.z += wq * v[u].z;
-        acc.w += wq * v[u].w;
-      }
+      const float wq = __shfl(wl, lg + 4 * u, kWave);  // 0 past the sequence
+      acc.x += wq * v[u].x;
+      acc.y += wq * v[u].y;
+      acc.z += wq * v[u].z;
+      acc.w += wq * v[u].w;
     }
   }
-  s_acc[rg][col] = acc;
-  __syncthreads();
-  if (tid < NCOL) {
-    float4 r = s_acc[0][tid];
+  wsum = group_sumf<kWave>(wsum);
+  float r[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
-    for (int g = 1; g < NR; ++g) {
-      r.x += s_acc[g][tid].x;
-      r.y += s_acc[g][tid].y;
-      r.z += s_acc[g][tid].z;
-      r.w += s_acc[g][tid].w;
-    }
+  for (int i = 0; i < 4; ++i) {
+    uint32_t x0, x1;
+    swap16(f_bits(r[i]), x0, x1);
+    r[i] = bits_f(x0) + bits_f(x1);
+    swap32(f_bits(r[i]), x0, x1);
+    r[i] = bits_f(x0) + bits_f(x1);
+  }
+  if (lane < 16) {
     const float inv = 1.0f / wsum;
-    r.x *= inv;
-    r.y *= inv;
-    r.z *= inv;
-    r.w *= inv;
-    reinterpret_cast<float4*>(a.out + ((size_t)s * a.num_q_heads + h) * D + 64 * slice)[tid] = r;
+    reinterpret_cast<float4*>(a.out + ((size_t)s * a.num_q_heads + h) * D + 64 * slice)[lane] =
+        make_float4(r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv);
   }
 }
 
@@ -409,7 +394,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG>), grid,                        \
                        dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                     \
     if (a.max_parts > 1)                                                                     \
-      hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(256), 0, stream, a);   \
+      hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(kWave), 0, stream, a); \
     return hipGetLastError();                                                                \
   }
   I8KV_DECODE_CASE(64, 32)
