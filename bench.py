@@ -215,6 +215,29 @@ def time_prefill(reps, G=32, graph=True):
     return dict(us=us, ops=ops, tops=ops / (us * 1e-6) / 1e12, workload=wl.name)
 
 
+DECODE_SOURCES = ["int8_kv_quantized_amd/csrc/decode.hip", "int8_kv_quantized_amd/csrc/kernels.hpp",
+                  "int8_kv_quantized_amd/csrc/device_common.hpp"]
+
+
+def counted_traffic(workload, G):
+    """HBM bytes per decode call from the committed FETCH_SIZE / WRITE_SIZE
+    counters (profiles/hbm_traffic.json), or None when no record matches the
+    workload or the decode kernel sources changed since they were taken."""
+    import hashlib
+    path = ROOT / "profiles" / "hbm_traffic.json"
+    if not path.exists():
+        return None
+    h = hashlib.sha256()
+    for s in DECODE_SOURCES:
+        h.update((ROOT / s).read_bytes())
+    for rec in json.loads(path.read_text()):
+        if (rec.get("workload") == workload and rec.get("w_group") == G
+                and rec.get("kernel_sources") == DECODE_SOURCES
+                and rec.get("kernel_sources_sha256") == h.hexdigest()):
+            return int(rec["hbm_bytes_per_call"])
+    return None
+
+
 def cpu_baseline(wl, G, seconds):
     """The oracle, single-threaded, on the same decode workload (whole calls)."""
     import numpy as np
@@ -330,7 +353,8 @@ def main():
                    "step": "kv_quantize_write(new token, with Q) + paged_decode_int8"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": counted_traffic(wl.name, args.w_group),
+                     "kernel": "paged_decode_int8 call (partition + merge kernels)"},
         "cpu_baseline": cpu,
         "extra": extra,
     }
