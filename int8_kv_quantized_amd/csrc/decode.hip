@@ -16,9 +16,11 @@
 // Two kernels, no cross-workgroup synchronization:
 //
 // 1. paged_decode_partition_kernel: one workgroup of 8 waves (4 for D = 64)
-//    per (256-token partition, KV head, sequence).  All K/V bytes of the
-//    partition are requested up front (16-byte loads, ~128 KiB in flight per
-//    workgroup), then:
+//    per (256-token partition, KV head, sequence).  Two load round trips:
+//    (1) sequence length, block-table entries, queries and their scales;
+//    (2) all scales and K bytes of the partition (16-byte loads), then each
+//    wave's V bytes as soon as its QK has consumed K (~128 KiB per workgroup
+//    in flight).  Then:
 //    * QK: v_mfma_i32_16x16x64_i8, A = the GQA group's int8 queries (rows =
 //      q heads, zero-padded to 16), B = one page: lane l holds the 16
 //      head-dim bytes of token l%16 in chunk 4c + l/16.  Wave w owns pages
@@ -153,8 +155,9 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   for (int g = 0; g < 4; ++g) pidv[g] = clamp_page(pidv[g]);
   pids = clamp_page(pids);
 
-  // ---- second round trip: every scale, K and V byte of the partition, issued
-  // in the order they are consumed (scales, K, V) so each wait is partial ----
+  // ---- second round trip: the scales and K bytes of the partition, then (once
+  // this wave's QK has consumed K, so V reuses its registers and K is not
+  // queued behind V) the V bytes; no load is conditional, each wait partial --
   float sk[PPW];
 #pragma unroll
   for (int j = 0; j < PPW; ++j) sk[j] = a.k_scale[((size_t)pidk[j] * kBlockSize + lr) * Hkv + kv];
@@ -169,6 +172,21 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
       kb[j][c] = *reinterpret_cast<const v4i*>(base + (4 * c + lg) * 256 + lr * 16);
   }
   __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < PPW; ++j)
+    if (tok0 + 16 * (w * PPW + j) + lr >= L) sk[j] = 0.0f;
+  if (tid < kPartition) s_sv[tid] = (tok0 + tid < L) ? sv_ld : 0.0f;
+
+  // ---- QK, the V loads, then scores -> LDS -------------------------------------
+  v4i qk[PPW];
+#pragma unroll
+  for (int j = 0; j < PPW; ++j) {
+    qk[j] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qk[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[c], kb[j][c], qk[j], 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   v4i vb[4][NCW];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -178,20 +196,6 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
       vb[g][c] = *reinterpret_cast<const v4i*>(base + (DecodeShape<D>::DW * w + 16 * c + lr) * 16);
   }
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int j = 0; j < PPW; ++j)
-    if (tok0 + 16 * (w * PPW + j) + lr >= L) sk[j] = 0.0f;
-  if (tid < kPartition) s_sv[tid] = (tok0 + tid < L) ? sv_ld : 0.0f;
-
-  // ---- QK, then scores -> LDS ----------------------------------------------
-  v4i qk[PPW];
-#pragma unroll
-  for (int j = 0; j < PPW; ++j) {
-    qk[j] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qk[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[c], kb[j][c], qk[j], 0, 0, 0);
-  }
 #pragma unroll
   for (int j = 0; j < PPW; ++j) {
     const int tl = 16 * (w * PPW + j) + lr;
