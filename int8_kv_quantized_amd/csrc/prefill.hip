@@ -18,6 +18,11 @@
 // 32 tokens x 6 heads for 24 q heads over 4 KV heads; wave w owns 16 rows and lane
 // l row l%16 (the four lanes l%16 + 16j share a row).  K/V tiles of 64 keys
 // are staged in LDS in their page layouts.
+//  * Tiles go from HBM straight into LDS (global_load_lds_dwordx4: one wave
+//    instruction moves 1 KiB, lane l landing at +16 l), double-buffered: the
+//    loads of tile t+1 are in flight while tile t is computed.  The source
+//    address of each lane is free, so the K tile is permuted inside every
+//    1 KiB piece while it is copied (see k_lds_off).
 //  * QK, transposed: S^T = K Q^T with v_mfma_i32_16x16x64_i8 (operand A = 16
 //    keys x 64 head-dim bytes from LDS, operand B = the int8 queries held in
 //    registers).  Two MFMA chains per 32-key group; their A rows read keys
@@ -66,21 +71,27 @@ __device__ __forceinline__ float row_sum4(float v) {
 
 }  // namespace
 
-// K tile row of one key: D bytes plus 16 of padding, and every 16-key block
-// shifted by 64 bytes more than the previous one.  With this layout the 16
-// keys one QK operand read touches (keys 8(r/4) + 4b + r%4 of a 32-key
-// group) hit 16 distinct 4-bank groups of the 64 LDS banks for D = 64, 128
-// and 256, and no two key rows overlap.
+// LDS layout of a K tile (4 pages of 16 keys): page j at j*(D*16 + 128), so odd
+// pages start 128 bytes into a 256-byte bank row; inside a page, 16-byte chunk
+// ch (head-dim bytes 16ch..16ch+15)
+// of all 16 keys at ch*256, key kp at slot kperm(kp).  kperm swaps keys 8..11
+// and 12..15 (an involution).  The 16 keys one QK operand read touches -- keys
+// {4b..4b+3, 8+4b..11+4b} of two consecutive pages -- then fill all sixteen
+// 16-byte slots of a 256-byte bank row, so the read has no bank conflict (the
+// previous padded layout measured two-way conflicts).
+__device__ __forceinline__ int kperm(int kp) { return kp ^ ((kp >> 3) << 2); }
+
 template <int D>
-__device__ __forceinline__ int k_lds_off(int key) {
-  return key * (D + 16) + ((key >> 4) << 6);
+__device__ __forceinline__ int k_lds_off(int key) {  // offset of chunk 0 of `key`
+  return (key >> 4) * (D * 16 + 128) + 16 * kperm(key & 15);
 }
 
 template <int D>
 struct PrefillTile {
-  static constexpr int kBytes = kKT * (D + 16) + (kKT / 16 - 1) * 64;  // K tile (padded)
-  static constexpr int vBytes = kKT / 16 * D * 16;    // V tile [page][dim][16]
-  static constexpr int kUnits = kKT / 16 * D;         // 16-byte units per operand
+  static constexpr int kBytes = kKT / 16 * (D * 16 + 128);  // K tile (pages 128 B apart)
+  static constexpr int vBytes = kKT / 16 * D * 16;        // V tile [page][dim][16]
+  static constexpr int kPieces = kKT / 16 * D * 16 / 1024;  // 1 KiB pieces per operand
+  static constexpr int kPagePieces = D * 16 / 1024;         // pieces per page
 };
 
 template <int D, int G>
@@ -89,8 +100,7 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
   constexpr int NN = D / 16;   // 16-dim output tiles of PV
   constexpr int NT = kNW * kWave;
   constexpr int KB = PrefillTile<D>::kBytes, VB = PrefillTile<D>::vBytes;
-  constexpr int UNITS = PrefillTile<D>::kUnits;
-  constexpr int UPT = (2 * UNITS + NT - 1) / NT;  // 16-byte units per thread per tile
+  constexpr int NPC = PrefillTile<D>::kPieces, PPP = PrefillTile<D>::kPagePieces;
   constexpr int kMaxBt = 4096;                    // block-table entries kept in LDS
 
   __shared__ __attribute__((aligned(16))) int8_t s_k[2][KB];
@@ -146,60 +156,52 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
     for (int i = tid; i < npages_used; i += NT)
       s_bt[i] = min(max(bt_row[i], 0), a.num_blocks - 1);
   __syncthreads();
+  // Page id of page pg of the sequence; pages past the keys in use map to page
+  // 0 of the cache (their keys are masked: score -inf, W 0).
   auto page_id = [&](int pg) -> int {
-    if (pg >= npages_used) return -1;
+    if (pg >= npages_used) return 0;
     return bt_in_lds ? s_bt[pg] : min(max(bt_row[pg], 0), a.num_blocks - 1);
   };
 
-  // ---- tile staging: global -> registers (next tile) -> LDS ------------------
-  v4i stg[UPT];
-  float stg_sk = 0.0f, stg_sv = 0.0f;
-  auto load_tile = [&](int t) {
+  // ---- tile loads: HBM -> LDS directly -----------------------------------------
+  // Wave w copies pieces w, w + kNW, ... of the 2 * NPC 1 KiB pieces of a tile
+  // (K pieces first, then V); the last two waves also copy the 64 K and V
+  // scales.  Lane l of a K piece fetches the key that belongs at slot l & 15.
+  const int koff_lane = (lane >> 4) * 256 + kperm(lane & 15) * 16;
+  auto issue_tile = [&](int t, int buf) {
     const int k0 = t * kKT;
-#pragma unroll
-    for (int j = 0; j < UPT; ++j) {
-      const int u = tid + j * NT;
-      stg[j] = v4i{0, 0, 0, 0};
-      if (u < 2 * UNITS) {
-        const int isv = u >= UNITS;
-        const int uu = isv ? u - UNITS : u;
-        const int pid = page_id(k0 / kBlockSize + uu / D);
-        if (pid >= 0)
-          stg[j] = *reinterpret_cast<const v4i*>((isv ? a.v_cache : a.k_cache) +
-                                                 ((size_t)pid * Hkv + kv) * (size_t)D * 16 +
-                                                 (size_t)(uu % D) * 16);
-      }
+    for (int q = w; q < 2 * NPC; q += kNW) {  // wave-uniform
+      const bool isv = q >= NPC;
+      const int qq = isv ? q - NPC : q;
+      const int j = qq / PPP, cp = qq % PPP;
+      const int pid = __builtin_amdgcn_readfirstlane(page_id(k0 / kBlockSize + j));
+      const size_t page = ((size_t)pid * Hkv + kv) * (size_t)D * 16 + (size_t)cp * 1024;
+      if (isv)
+        __builtin_amdgcn_global_load_lds(a.v_cache + page + lane * 16,
+                                         (__attribute__((address_space(3))) void*)
+                                             (s_v[buf] + j * D * 16 + cp * 1024),
+                                         16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(a.k_cache + page + koff_lane,
+                                         (__attribute__((address_space(3))) void*)
+                                             (s_k[buf] + j * (D * 16 + 128) + cp * 1024),
+                                         16, 0, 0);
     }
-    if (tid < kKT) {
-      const int key = k0 + tid;
-      const int pid = page_id(key / kBlockSize);
-      stg_sk = stg_sv = 0.0f;
-      if (pid >= 0 && key < seq_len) {
-        const size_t idx = ((size_t)pid * kBlockSize + (tid % 16)) * Hkv + kv;
-        stg_sk = a.k_scale[idx];
-        stg_sv = a.v_scale[idx];
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < UPT; ++j) {
-      const int u = tid + j * NT;
-      if (u < 2 * UNITS) {
-        if (u >= UNITS) {
-          const int uu = u - UNITS;  // V: page uu / D, dim uu % D
-          *reinterpret_cast<v4i*>(&s_v[buf][uu * 16]) = stg[j];
-        } else {  // K: page u / D, chunk (u % D) / 16, key in page u % 16
-          const int key = 16 * (u / D) + (u % 16);
-          *reinterpret_cast<v4i*>(&s_k[buf][k_lds_off<D>(key) + 16 * ((u % D) / 16)]) = stg[j];
-        }
-      }
-    }
-    if (tid < kKT) {
-      s_sk[buf][tid] = stg_sk;
-      s_sv[buf][tid] = stg_sv;
+    if (w >= kNW - 2) {  // scale of key k0 + lane (keys past the sequence: any finite
+                         // or not value, discarded by the masked path)
+      const int pid = page_id((k0 + lane) / kBlockSize);
+      const size_t idx = ((size_t)pid * kBlockSize + (lane % 16)) * Hkv + kv;
+      if (w == kNW - 1)
+        __builtin_amdgcn_global_load_lds(a.k_scale + idx,
+                                         (__attribute__((address_space(3))) void*)s_sk[buf], 4, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(a.v_scale + idx,
+                                         (__attribute__((address_space(3))) void*)s_sv[buf], 4, 0, 0);
     }
   };
+  // every copy of this wave has landed in LDS (the barrier that follows makes
+  // all waves' copies visible)
+  auto wait_tile = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   float mref = row_ok ? -INFINITY : INFINITY;  // reference max (log2 units)
   float lsum = 0.0f;                           // this lane's share of l
@@ -224,10 +226,10 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
       for (int b = 0; b < 2; ++b) {
         acc[b] = v4i{0, 0, 0, 0};
         const int krow = 32 * g + 8 * (lr >> 2) + 4 * b + (lr & 3);  // key of A row lr
-        const int8_t* kp = kt + k_lds_off<D>(krow) + 16 * lg;
+        const int8_t* kp = kt + k_lds_off<D>(krow) + 256 * lg;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const v4i ka = *reinterpret_cast<const v4i*>(kp + 64 * c);
+          const v4i ka = *reinterpret_cast<const v4i*>(kp + 1024 * c);
           acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qb[c], acc[b], 0, 0, 0);
         }
       }
@@ -266,9 +268,17 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
       float mx = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pt = __builtin_amdgcn_exp2f(__builtin_fmaf(u2[g][j], crow, -mref));
-        lsum += pt;
+        float pt = __builtin_amdgcn_exp2f(__builtin_fmaf(u2[g][j], crow, -mref));
         Wv[g][j] = pt * svv[j];
+        if constexpr (MASK) {
+          // a masked key has p~ = 0 and W = 0 whatever its score constant
+          // (crow = 0 for an all-zero query) or scale (any value past the
+          // sequence) would give
+          const bool vis = k0 + 32 * g + 8 * lg + j <= pos;
+          pt = vis ? pt : 0.0f;
+          Wv[g][j] = vis ? Wv[g][j] : 0.0f;
+        }
+        lsum += pt;
         mx = fmaxf(mx, Wv[g][j]);
       }
       am[g] = row_max4(mx);
@@ -320,18 +330,18 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
     }
   };
 
-  load_tile(0);
-  store_tile(0);
+  issue_tile(0, 0);
+  wait_tile();
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int k0 = t * kKT;
-    if (t + 1 < ntiles) load_tile(t + 1);  // in flight during this tile's compute
+    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);  // in flight during this tile's compute
     if (k0 < wave_nkeys) {
       if (k0 + kKT - 1 > wave_min_pos) compute_tile(buf, k0, std::true_type{});
       else compute_tile(buf, k0, std::false_type{});
     }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    wait_tile();
     __syncthreads();
   }
 

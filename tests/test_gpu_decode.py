@@ -85,6 +85,19 @@ def test_decode_empty_sequence(orc):
     assert_close(out, ref, "empty")
 
 
+@pytest.mark.parametrize("G", [32, 64])
+def test_decode_zero_vectors(orc, G):
+    """All-zero query vectors (sQ = 0: uniform softmax over the sequence) and
+    all-zero key / value vectors (scale 0)."""
+    wl = W.make_workload("zero_vectors", seq_lens=(700, 300, 40), new_tokens=[1, 1, 1],
+                         num_q_heads=6, num_kv_heads=2, head_dim=128, seed=53, w_group=G)
+    wl.query[0] = 0              # every head of the first sequence's query
+    wl.query[1, 3] = 0           # one head of the second
+    wl.key[::9, 0] = 0
+    wl.value[5::17, 1] = 0
+    run_decode(wl, orc, G)
+
+
 @pytest.mark.parametrize("G", [32])
 def test_decode_cfg1_L512(orc, G):
     run_decode(W.cfg1_decode_512(G), orc, G)

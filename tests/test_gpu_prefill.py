@@ -70,3 +70,17 @@ def test_prefill_cfg4_sampled(orc, G):
     rows = sorted(set([0, 1, 21, 22, 127, 128, 1023, 2046, 2047]
                       + rng.integers(0, 2048, 7).tolist()))
     run_prefill(wl, orc, G, rows=rows)
+
+
+@pytest.mark.parametrize("G", [32, 64])
+def test_prefill_zero_vectors(orc, G):
+    """All-zero query vectors (sQ = 0: every visible score 0, a uniform softmax)
+    and all-zero key / value vectors (scale 0) inside the chunk and history."""
+    wl = W.make_workload("zero_vectors", seed=67, kind="prefill", w_group=G,
+                         seq_lens=(150, 90), new_tokens=(70, 90), num_q_heads=6,
+                         num_kv_heads=2, head_dim=128)
+    wl.query[::5, :, :] = 0          # every fifth query token, all heads
+    wl.query[1::7, 2, :] = 0         # one head of others
+    wl.key[::11, 1, :] = 0           # some keys of KV head 1
+    wl.value[3::13, 0, :] = 0        # some values of KV head 0
+    run_prefill(wl, orc, G)
