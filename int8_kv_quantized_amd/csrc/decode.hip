@@ -227,25 +227,25 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
     }
     ls = group_sum<kWave>(ls);
     const float l = (float)ls;
-    const double rl = 1.0 / (double)l;
+    const double rl = rcp_f64((double)l);  // l >= 1 (the max term is exp(0) = 1)
     const float4 v4 = *reinterpret_cast<const float4*>(&s_sv[4 * lane]);
     const float sv[4] = {v4.x, v4.y, v4.z, v4.w};
     float W[4];
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float P = div_f32_rn(e[i], rl);  // == e / l (IEEE)
+      const float P = div_f32_rn(e[i], l, rl);  // == e / l (IEEE)
       W[i] = P * sv[i];
       am = fmaxf(am, W[i]);
     }
     am = group_max<G / 4>(am);  // G consecutive tokens = G/4 consecutive lanes
-    const float sw = am / 127.0f;
+    const float sw = div_f32_rn(am, 127.0f, 1.0 / 127.0);  // == am / 127 (IEEE)
     uint32_t packed = 0;
-    if (am > 0.0f) {
-      const double rsw = 1.0 / (double)sw;
+    if (sw > 0.0f) {  // sW = 0 (also when max W / 127 underflows): the group adds 0
+      const double rsw = rcp_f64((double)sw);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        packed |= (uint32_t)(round_code(div_f32_rn(W[i], rsw)) & 0xff) << (8 * i);
+        packed |= (uint32_t)(round_code(div_f32_rn(W[i], sw, rsw)) & 0xff) << (8 * i);
     }
     *reinterpret_cast<uint32_t*>(&s_wq[h * kWqStride + 4 * lane]) = packed;
     if (((4 * lane) & (G - 1)) == 0) s_sw[h][(4 * lane) / G] = sw;

@@ -32,12 +32,27 @@ __device__ __forceinline__ int round_code(float q) {
   return (int)fminf(fmaxf(roundf(q), -127.0f), 127.0f);
 }
 
-// The IEEE fp32 quotient a / b from rb = 1/b rounded to fp64.  The quotient
-// of two fp32 values is never an fp32 rounding midpoint and lies at least
-// about 2^-50 (relative) away from one, while a * rb carries a relative error
-// below 2^-52, so rounding it to fp32 gives the correctly rounded quotient.
-__device__ __forceinline__ float div_f32_rn(float a, double rb) {
-  return (float)((double)a * rb);
+// The IEEE fp32 quotient a / b, given rb ~ 1/b in fp64 (relative error below
+// 2^-51).  When a / b is a normal fp32 number it is never a rounding midpoint
+// and lies at least ~2^-49 (relative) away from one, while a * rb carries a
+// relative error below 2^-50.5, so rounding a * rb to fp32 gives the correctly
+// rounded quotient.  A quotient in the fp32 subnormal range can be an exact
+// midpoint of the coarser subnormal grid, so there the IEEE division is done.
+__device__ __forceinline__ float div_f32_rn(float a, float b, double rb) {
+  const double q = (double)a * rb;
+  if (__builtin_fabs(q) < 0x1p-126) return a / b;
+  return (float)q;
+}
+
+// 1/x for a positive, finite, normal fp64 x: the hardware estimate refined by
+// two Newton steps, r' = r + r (1 - x r).  The result is within ~1 ulp of 1/x,
+// well inside the 2^-51 that div_f32_rn needs; x = 0 gives a non-finite value.
+__device__ __forceinline__ double rcp_f64(double x) {
+  double r = __builtin_amdgcn_rcp(x);
+  double e = __builtin_fma(-x, r, 1.0);
+  r = __builtin_fma(r, e, r);
+  e = __builtin_fma(-x, r, 1.0);
+  return __builtin_fma(r, e, r);
 }
 
 // ---- cross-lane reductions inside aligned groups of `width` lanes ----------
