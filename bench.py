@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the int8-KV paged-attention hot path on one MI355X.
 
-A step is one pass of the hot path over one batch: the fused producer
-quantizes and writes the new token's K/V (and its query) into the paged int8
-cache, then paged decode attends over the whole history.  The default
+A step is one pass of the hot path over one batch: the producer quantizes
+and writes the new token's K/V (and its query) into the paged int8 cache and
+paged decode attends over the whole history -- by default as the fused
+decode_step_int8 call (one decode launch), with the two separate calls
+(kv_quantize_write + paged_decode_int8) timed beside it.  The default
 workload is decode at 16384 tokens of history (batch 1, 24 q / 4 KV heads,
 head_dim 256, page 16, 1% of V channels x20, W group 32), with inputs
 resident in HBM and rotated over enough distinct cache copies (>= 512 MB) to
@@ -51,6 +53,9 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--sweep", action="store_true",
                    help="also time every decode configuration and prefill at G=32/64")
+    p.add_argument("--separate-step", action="store_true",
+                   help="time the step as kv_quantize_write + paged_decode_int8 instead of "
+                        "the fused decode_step_int8")
     p.add_argument("--no-graph", action="store_true",
                    help="launch eagerly instead of replaying HIP graphs (for counter runs)")
     p.add_argument("--copy-calibration-mb", type=float, default=0.0,
@@ -121,9 +126,16 @@ def time_decode(args, log_prefix=""):
         K.paged_decode_int8(d, dq8, dqs, caches[i % copies], bt, sl, wl.max_seq_len,
                             w_group=args.w_group, workspace=ws, out=out)
 
-    def step(i):
+    def step_separate(i):
         producer(i)
         decode(i)
+
+    def step_fused(i):  # the same work as step_separate, in one decode launch
+        K.decode_step_int8(d, knew, vnew, qnew, caches[i % copies], bt, sl, wl.max_seq_len,
+                           w_group=args.w_group, workspace=ws, out=out, q_int8=q8, q_scale=qs)
+
+    fused = per_seq == 1 and not args.separate_step
+    step = step_fused if fused else step_separate
 
     # Launch-bound at these sizes: capture whole loops in HIP graphs so the
     # timed region is the GPU's work, not the Python launch rate.
@@ -156,14 +168,17 @@ def time_decode(args, log_prefix=""):
 
     g_warm = capture(step, max(args.warmup, 1))
     g_step = capture(step, args.steps)
+    g_sep = capture(step_separate, args.steps) if fused else g_step
     g_dec = capture(decode, args.steps)
     g_prod = capture(producer, args.steps)
     if args.warmup:
         replay_ms(g_warm)
     ms_total = replay_ms(g_step)
+    sep_ms = replay_ms(g_sep) / args.steps if fused else ms_total / args.steps
     dec_ms = [replay_ms(g_dec) / args.steps for _ in range(3)]
     prod_ms = [replay_ms(g_prod) / args.steps for _ in range(3)]
-    return dict(wl=wl, desc=d, copies=copies, ms_per_step=ms_total / args.steps,
+    return dict(wl=wl, desc=d, copies=copies, ms_per_step=ms_total / args.steps, fused=fused,
+                step_separate_us=1e3 * sep_ms,
                 producer_us=1e3 * float(np.median(prod_ms)),
                 decode_us=1e3 * float(np.median(dec_ms)), decode_us_runs=[1e3 * x for x in dec_ms])
 
@@ -299,8 +314,9 @@ def main():
         f"{r['producer_us']:.2f} us, step {r['ms_per_step'] * 1e3:.2f} us, "
         f"{achieved:.0f} GB/s effective ({100 * achieved / HBM_PEAK_GBS:.1f}% of peak)")
     extra = dict(decode_us=round(r["decode_us"], 3),
-                 producer_us=round(r["producer_us"], 3), effective_kv_bytes=eff,
-                 cache_copies_rotated=r["copies"])
+                 producer_us=round(r["producer_us"], 3),
+                 step_separate_calls_us=round(r["step_separate_us"], 3),
+                 effective_kv_bytes=eff, cache_copies_rotated=r["copies"])
     if not args.no_prefill:
         pf = time_prefill(args.prefill_reps, graph=not args.no_graph)
         log(f"prefill {pf['workload']}: {pf['us']:.1f} us, {pf['tops']:.1f} int8 TOPS "
@@ -320,6 +336,7 @@ def main():
                 sweep[f"{name}_G{G}"] = dict(
                     decode_us=round(rr["decode_us"], 3), producer_us=round(rr["producer_us"], 3),
                     step_us=round(rr["ms_per_step"] * 1e3, 3),
+                    step_separate_calls_us=round(rr["step_separate_us"], 3),
                     decode_gbs=round(b / (rr["decode_us"] * 1e-6) / 1e9, 1),
                     decode_frac_hbm=round(b / (rr["decode_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
                 log(f"  sweep {name} G={G}: {sweep[f'{name}_G{G}']}")
@@ -350,7 +367,9 @@ def main():
                    "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "page_size": 16, "w_group": args.w_group,
                    "partition": 256,
-                   "step": "kv_quantize_write(new token, with Q) + paged_decode_int8"},
+                   "step": ("decode_step_int8 (producer of the new token, with Q, fused "
+                            "into paged decode)" if r["fused"] else
+                            "kv_quantize_write(new token, with Q) + paged_decode_int8")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": counted_traffic(wl.name, args.w_group),

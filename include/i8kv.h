@@ -1,7 +1,7 @@
 /*
  * i8kv -- paged attention over an INT8 KV cache, native to AMD MI355X (gfx950).
  *
- * C ABI of the library libi8kv.so.  Three operations, as defined on the pages
+ * C ABI of the library libi8kv.so.  Four calls, on the operations defined on the pages
  *   [KV] "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
  *        DCU" (part 1 of the series), and
  *   [PV] "Implementing INT8 PV MMAC on a gfx936 DCU: V-scale fusion,
@@ -12,6 +12,8 @@
  *                              [PV] 2.2, merge by log-sum-exp weights)
  *   i8kv_prefix_prefill_int8 -- chunked prefill with history in one online
  *                              softmax ([KV] 3.2, [PV] 2.1)
+ *   i8kv_decode_step_int8   -- the producer of each sequence's newest token
+ *                              fused into the decode of that token
  *
  * Conventions for every call
  *  - Tensor arguments are DEVICE pointers owned by the caller, C-contiguous in
@@ -132,6 +134,35 @@ i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs
                                    float softmax_scale, void* workspace,
                                    size_t workspace_bytes, float* out,
                                    i8kv_stream_t stream);
+
+/*
+ * One decode step with the producer fused in: for every sequence s, the
+ * newest token (position seq_lens[s] - 1) is quantized and written to the
+ * cache as i8kv_kv_quantize_write would write it ([KV] 2.1-2.3, with its slot
+ * taken from block_tables), its query is quantized once ([KV] 2.2), and the
+ * token's query attends to all seq_lens[s] tokens exactly as
+ * i8kv_paged_decode_int8 computes it ([KV] 3.3; [PV] 2.2).  Caches, scales,
+ * q_int8 / q_scale and out are bit-identical to those two calls in sequence;
+ * the step is one partition kernel (plus the merge kernel) instead of three
+ * kernels.
+ *   key, value   [S, Hkv, D] bf16      query [S, Hq, D] bf16 (the newest tokens)
+ *   q_int8 [S, Hq, D], q_scale [S, Hq]: optional outputs (both NULL or both set)
+ *   caches as for i8kv_kv_quantize_write; the page of position seq_lens[s] - 1
+ *   is block_tables[s][(seq_lens[s] - 1) / 16] (an entry outside [0, num_blocks)
+ *   skips the write, as a negative slot does for the producer); a sequence
+ *   with seq_lens[s] = 0 writes no token and outputs zeros.
+ *   Other arguments, workspace and errors as for i8kv_paged_decode_int8
+ *   (NULL also for a missing key/value/query or only one of q_int8/q_scale).
+ */
+i8kv_status i8kv_decode_step_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                  const uint16_t* key, const uint16_t* value,
+                                  const uint16_t* query, int8_t* q_int8, float* q_scale,
+                                  int8_t* k_cache, int8_t* v_cache, float* k_scale,
+                                  float* v_scale, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  int32_t max_seq_len, int32_t partition_size, int32_t w_group,
+                                  float softmax_scale, void* workspace, size_t workspace_bytes,
+                                  float* out, i8kv_stream_t stream);
 
 /* Workspace bytes for i8kv_prefix_prefill_int8 (currently none needed). */
 size_t i8kv_prefix_prefill_workspace_bytes(const i8kv_cache_desc* desc, int32_t num_seqs,

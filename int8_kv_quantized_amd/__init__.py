@@ -11,12 +11,14 @@ fails loudly if the library has not been built -- there is no fallback.
     paged_decode_int8(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
     prefix_prefill_int8(desc, q_int8, q_scale, query_start_loc, seq_lens,
                         cache, block_tables, ...)
+    decode_step_int8(desc, key, value, query, cache, block_tables, seq_lens, ...)
 """
 from ._binding import (  # noqa: F401
     CacheDesc,
     I8KVError,
     PagedCache,
     abi_version,
+    decode_step_int8,
     kv_quantize_write,
     lib_path,
     load_library,

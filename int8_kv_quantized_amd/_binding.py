@@ -72,6 +72,9 @@ def load_library():
     lib.i8kv_paged_decode_int8.restype = C.c_int
     lib.i8kv_paged_decode_int8.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F, P, SZ,
                                                                  P, P])
+    lib.i8kv_decode_step_int8.restype = C.c_int
+    lib.i8kv_decode_step_int8.argtypes = ([D, I32] + [P] * 10 + [I32, P, I32, I32, I32, F, P, SZ,
+                                                                  P, P])
     lib.i8kv_prefix_prefill_workspace_bytes.restype = SZ
     lib.i8kv_prefix_prefill_workspace_bytes.argtypes = [D, I32, I32]
     lib.i8kv_prefix_prefill_int8.restype = C.c_int
@@ -252,6 +255,54 @@ def paged_decode_int8(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block
         int(w_group), float(softmax_scale), _ptr(workspace), int(ws_bytes), _ptr(out),
         _stream(stream))
     _raise("paged_decode_int8", st)
+    return out
+
+
+def decode_step_int8(desc: CacheDesc, key, value, query, cache: PagedCache, block_tables,
+                     seq_lens, max_seq_len: int, w_group: int = 32, partition_size: int = 256,
+                     softmax_scale: Optional[float] = None, workspace=None, out=None,
+                     q_int8=None, q_scale=None, stream=None):
+    """One decode step with the producer fused in: writes each sequence's
+    newest token (position seq_lens[s] - 1, bf16 ``key``/``value`` [S, Hkv, D])
+    into ``cache`` and attends its ``query`` [S, Hq, D] over the sequence.
+    Returns ``out`` [S, Hq, D] fp32; ``q_int8``/``q_scale`` are optional
+    outputs (the quantized queries)."""
+    import torch
+    lib = load_library()
+    S = int(seq_lens.shape[0]) if _is_tensor(seq_lens) else int(key.shape[0])
+    Hq, Hkv, D = desc.num_q_heads, desc.num_kv_heads, desc.head_dim
+    bits16 = (torch.bfloat16, torch.int16, torch.uint16)
+    _check(key, "key", bits16, (S, Hkv, D))
+    _check(value, "value", bits16, (S, Hkv, D))
+    _check(query, "query", bits16, (S, Hq, D))
+    if (q_int8 is None) != (q_scale is None):
+        raise ValueError("q_int8 and q_scale go together")
+    if q_int8 is not None:
+        _check(q_int8, "q_int8", torch.int8, (S, Hq, D))
+        _check(q_scale, "q_scale", torch.float32, (S, Hq))
+    cache.check(desc)
+    _check(block_tables, "block_tables", torch.int32)
+    if not _is_tensor(block_tables):
+        raise ValueError("block_tables must be a tensor (its width is needed)")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError(f"block_tables: shape {tuple(block_tables.shape)}, expected ({S}, *)")
+    _check(seq_lens, "seq_lens", torch.int32, (S,))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    need = paged_decode_workspace_bytes(desc, S, max_seq_len, partition_size)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=block_tables.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if _is_tensor(workspace) else need
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=block_tables.device)
+    _check(out, "out", torch.float32, (S, Hq, D))
+    st = lib.i8kv_decode_step_int8(
+        C.byref(desc), S, _ptr(key), _ptr(value), _ptr(query), _ptr(q_int8), _ptr(q_scale),
+        _ptr(cache.k_cache), _ptr(cache.v_cache), _ptr(cache.k_scale), _ptr(cache.v_scale),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len),
+        int(partition_size), int(w_group), float(softmax_scale), _ptr(workspace), int(ws_bytes),
+        _ptr(out), _stream(stream))
+    _raise("decode_step_int8", st)
     return out
 
 

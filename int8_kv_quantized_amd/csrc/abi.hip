@@ -97,28 +97,39 @@ size_t i8kv_paged_decode_workspace_bytes(const i8kv_cache_desc* desc, int32_t nu
   return p.bytes;
 }
 
-i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
-                                   const int8_t* q_int8, const float* q_scale,
-                                   const int8_t* k_cache, const int8_t* v_cache,
-                                   const float* k_scale, const float* v_scale,
-                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                   const int32_t* seq_lens, int32_t max_seq_len,
-                                   int32_t partition_size, int32_t w_group,
-                                   float softmax_scale, void* workspace,
-                                   size_t workspace_bytes, float* out,
-                                   i8kv_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the decode and the fused decode-step entry points: validation and
+// argument packing, then the launch.  `fused` carries the producer inputs and
+// outputs of the step (new_key non-null), with q_int8 / q_scale then optional
+// outputs rather than inputs.
+i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8_t* q_int8,
+                       const float* q_scale, const int8_t* k_cache, const int8_t* v_cache,
+                       const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                       int32_t partition_size, int32_t w_group, float softmax_scale,
+                       void* workspace, size_t workspace_bytes, float* out,
+                       const DecodeArgs* fused, i8kv_stream_t stream) {
   i8kv_status st = check_desc(desc);
   if (st != I8KV_OK) return st;
-  if (!q_int8 || !q_scale || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables ||
-      !seq_lens || !out)
+  if (!k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !seq_lens || !out)
     return I8KV_ERR_NULL;
+  if (!fused && (!q_int8 || !q_scale)) return I8KV_ERR_NULL;
+  if (fused && (!fused->new_key || !fused->new_value || !fused->new_query)) return I8KV_ERR_NULL;
+  if (fused && (!q_int8) != (!q_scale)) return I8KV_ERR_NULL;
   if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq <= 0) return I8KV_ERR_INVALID_ARG;
   if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * kBlockSize) return I8KV_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return I8KV_ERR_INVALID_ARG;
   if (partition_size != kPartition || (w_group != 32 && w_group != 64))
     return I8KV_ERR_UNSUPPORTED;
   if (max_seq_len > kMaxSeqLen || num_seqs > kMaxGridYZ) return I8KV_ERR_UNSUPPORTED;
-  if (!aligned16(q_int8) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+  if ((q_int8 && !aligned16(q_int8)) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(out))
+    return I8KV_ERR_INVALID_ARG;
+  if (fused && (!aligned16(fused->new_key) || !aligned16(fused->new_value) ||
+                !aligned16(fused->new_query)))
     return I8KV_ERR_INVALID_ARG;
   if (num_seqs == 0) return I8KV_OK;
   const int32_t grp = desc->num_q_heads / desc->num_kv_heads;
@@ -129,6 +140,7 @@ i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs
 
   char* ws = static_cast<char*>(workspace);
   DecodeArgs a{};
+  if (fused) a = *fused;  // producer pointers of the fused step
   a.num_seqs = num_seqs;
   a.num_q_heads = desc->num_q_heads;
   a.num_kv_heads = desc->num_kv_heads;
@@ -139,8 +151,8 @@ i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs
   a.max_seq_len = max_seq_len;
   a.w_group = w_group;
   a.softmax_scale = softmax_scale;
-  a.q_int8 = q_int8;
-  a.q_scale = q_scale;
+  a.q_int8 = fused ? nullptr : q_int8;
+  a.q_scale = fused ? nullptr : q_scale;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.k_scale = k_scale;
@@ -152,6 +164,49 @@ i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs
   a.part_ml = reinterpret_cast<float*>(ws + p.off_part_ml);
   a.max_parts = p.max_parts;
   return from_hip(launch_paged_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                   const int8_t* q_int8, const float* q_scale,
+                                   const int8_t* k_cache, const int8_t* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* seq_lens, int32_t max_seq_len,
+                                   int32_t partition_size, int32_t w_group,
+                                   float softmax_scale, void* workspace,
+                                   size_t workspace_bytes, float* out,
+                                   i8kv_stream_t stream) {
+  return run_decode(desc, num_seqs, q_int8, q_scale, k_cache, v_cache, k_scale, v_scale,
+                    block_tables, max_blocks_per_seq, seq_lens, max_seq_len, partition_size,
+                    w_group, softmax_scale, workspace, workspace_bytes, out, nullptr, stream);
+}
+
+i8kv_status i8kv_decode_step_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                  const uint16_t* key, const uint16_t* value,
+                                  const uint16_t* query, int8_t* q_int8, float* q_scale,
+                                  int8_t* k_cache, int8_t* v_cache, float* k_scale,
+                                  float* v_scale, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  int32_t max_seq_len, int32_t partition_size, int32_t w_group,
+                                  float softmax_scale, void* workspace, size_t workspace_bytes,
+                                  float* out, i8kv_stream_t stream) {
+  DecodeArgs f{};
+  f.new_key = key;
+  f.new_value = value;
+  f.new_query = query;
+  f.k_cache_w = k_cache;
+  f.v_cache_w = v_cache;
+  f.k_scale_w = k_scale;
+  f.v_scale_w = v_scale;
+  f.q_int8_w = q_int8;
+  f.q_scale_w = q_scale;
+  return run_decode(desc, num_seqs, q_int8, q_scale, k_cache, v_cache, k_scale, v_scale,
+                    block_tables, max_blocks_per_seq, seq_lens, max_seq_len, partition_size,
+                    w_group, softmax_scale, workspace, workspace_bytes, out, &f, stream);
 }
 
 size_t i8kv_prefix_prefill_workspace_bytes(const i8kv_cache_desc* desc, int32_t num_seqs,

@@ -76,7 +76,7 @@ struct DecodeShape {
   static constexpr int NCW = DW / 16;          // 16-dim PV tiles per wave
 };
 
-template <int D, int G>
+template <int D, int G, bool FUSED>
 __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_partition_kernel(
     DecodeArgs a) {
   constexpr int NW = DecodeShape<D>::NW;
@@ -91,6 +91,10 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   __shared__ __attribute__((aligned(16))) float s_sv[kPartition];
   __shared__ float s_sw[16][NGP];
   __shared__ float s_M[16], s_L[16];
+  // fused step: the group's quantized queries and the newest token's K/V codes
+  __shared__ __attribute__((aligned(16))) int8_t s_q[FUSED ? 16 : 1][FUSED ? D : 16];
+  __shared__ __attribute__((aligned(16))) int8_t s_nk[FUSED ? D : 16], s_nv[FUSED ? D : 16];
+  __shared__ float s_qs[16], s_nsc[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -114,7 +118,25 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   for (int g = 0; g < 4; ++g) pidv[g] = bt_at(4 * g + lg);      // V pages of this lane
   int pids = bt_at(tsv >> 4);
   v4i qa[NC];
-  {
+  float sq[4];
+  // Fused step: wave w quantizes items w, w + NW, ... of the group's grp q
+  // heads followed by the newest token's K (item grp) and V (item grp + 1);
+  // their bf16 inputs are part of this round trip.
+  constexpr int kMaxItems = (16 + 2 + NW - 1) / NW;
+  uint2 raw[kMaxItems];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int k = 0; k < kMaxItems; ++k) {
+      const int it = wu + k * NW;
+      raw[k] = make_uint2(0u, 0u);
+      if (it < grp)
+        raw[k] = load_wave_vector<D>(
+            a.new_query + ((size_t)s * a.num_q_heads + (size_t)kv * grp + it) * D, lane);
+      else if (it < grp + 2)
+        raw[k] = load_wave_vector<D>(
+            (it == grp ? a.new_key : a.new_value) + ((size_t)s * Hkv + kv) * D, lane);
+    }
+  } else {
     const bool vh = lr < grp;
     const int8_t* qp = a.q_int8 +
                        ((size_t)s * a.num_q_heads + (size_t)kv * grp + (vh ? lr : 0)) * D + 16 * lg;
@@ -123,13 +145,12 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
       qa[c] = *reinterpret_cast<const v4i*>(qp + 64 * c);
       if (!vh) qa[c] = v4i{0, 0, 0, 0};
     }
-  }
-  float sq[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * lg + r;
-    sq[r] = a.q_scale[(size_t)s * a.num_q_heads + (size_t)kv * grp + min(h, grp - 1)];
-    if (h >= grp) sq[r] = 0.0f;
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * lg + r;
+      sq[r] = a.q_scale[(size_t)s * a.num_q_heads + (size_t)kv * grp + min(h, grp - 1)];
+      if (h >= grp) sq[r] = 0.0f;
+    }
   }
 
   // keep the loads above ahead of the early exits below (the compiler would
@@ -139,6 +160,47 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   const int L = min(max(L_raw, 0), a.max_seq_len);
   const int P_s = (L + kPartition - 1) / kPartition;
   float* out_base = a.out + ((size_t)s * a.num_q_heads + (size_t)kv * grp) * D;
+  // the newest token (position L - 1) lives in the sequence's last partition
+  const bool newest_here = FUSED && L > 0 && p == P_s - 1;
+  if constexpr (FUSED) {
+    if (p < max(P_s, 1)) {
+      constexpr int EPL = D / kWave;
+#pragma unroll
+      for (int k = 0; k < kMaxItems; ++k) {
+        const int it = wu + k * NW;
+        if (it >= grp + 2 || (it >= grp && !newest_here)) continue;  // wave-uniform
+        float sc;
+        const uint32_t codes = quantize_wave_vector<D>(raw[k], sc);
+        int8_t* lds = it < grp ? s_q[it] : (it == grp ? s_nk : s_nv);
+        if constexpr (EPL == 4) *reinterpret_cast<uint32_t*>(lds + lane * 4) = codes;
+        else if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(lds + lane * 2) = (uint16_t)codes;
+        else lds[lane] = (int8_t)codes;
+        if (it < grp) {
+          if (lane == 0) s_qs[it] = sc;
+          if (p == 0 && a.q_int8_w) {  // the producer's Q outputs, written once
+            const size_t qrow = (size_t)s * a.num_q_heads + (size_t)kv * grp + it;
+            int8_t* dst = a.q_int8_w + qrow * D + lane * EPL;
+            if constexpr (EPL == 4) *reinterpret_cast<uint32_t*>(dst) = codes;
+            else if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)codes;
+            else *dst = (int8_t)codes;
+            if (lane == 0) a.q_scale_w[qrow] = sc;
+          }
+        } else {
+          // the producer's cache write of the newest token (slot from the table)
+          if (lane == 0) s_nsc[it - grp] = sc;
+          const int pos = L - 1;
+          const int blk = bt_row[min(pos / kBlockSize, a.max_blocks_per_seq - 1)];
+          if (blk >= 0 && blk < a.num_blocks) {
+            const int off = pos % kBlockSize;
+            if (it == grp) store_k_token<D>(a.k_cache_w, blk, kv, Hkv, off, lane, codes);
+            else store_v_token<D>(a.v_cache_w, blk, kv, Hkv, off, lane, codes);
+            if (lane == 0)
+              (it == grp ? a.k_scale_w : a.v_scale_w)[((size_t)blk * kBlockSize + off) * Hkv + kv] = sc;
+          }
+        }
+      }
+    }
+  }
   if (L == 0) {
     if (p == 0)
       for (int i = tid; i < grp * D; i += NT) out_base[i] = 0.0f;
@@ -176,6 +238,28 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   for (int j = 0; j < PPW; ++j)
     if (tok0 + 16 * (w * PPW + j) + lr >= L) sk[j] = 0.0f;
   if (tid < kPartition) s_sv[tid] = (tok0 + tid < L) ? sv_ld : 0.0f;
+
+  const int t_new = L - 1 - tok0;  // newest token within the partition (if newest_here)
+  if constexpr (FUSED) {
+    __syncthreads();  // s_q, s_qs, s_nk, s_nv, s_nsc
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qa[c] = lr < grp ? *reinterpret_cast<const v4i*>(&s_q[lr][64 * c + 16 * lg]) : v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sq[r] = 4 * lg + r < grp ? s_qs[4 * lg + r] : 0.0f;
+    if (newest_here) {
+      // this thread's K registers and V scale slot may hold the cache contents
+      // from before the write above: use the new token's codes and scales
+#pragma unroll
+      for (int j = 0; j < PPW; ++j)
+        if (16 * (w * PPW + j) + lr == t_new) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) kb[j][c] = *reinterpret_cast<const v4i*>(&s_nk[64 * c + 16 * lg]);
+          sk[j] = s_nsc[0];
+        }
+      if (tid == t_new) s_sv[tid] = s_nsc[1];
+    }
+  }
 
   // ---- QK, the V loads, then scores -> LDS -------------------------------------
   v4i qk[PPW];
@@ -255,6 +339,23 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
     }
   }
   __syncthreads();
+
+  if (FUSED && newest_here) {
+    // V bytes of the newest token (byte t_new % 16 of the 16-token rows of
+    // page t_new / 16) from the codes quantized above
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      if (4 * g + lg == t_new / 16) {
+        const int bsel = t_new % 16;
+#pragma unroll
+        for (int c = 0; c < NCW; ++c) {
+          const uint32_t code = (uint8_t)s_nv[DecodeShape<D>::DW * w + 16 * c + lr];
+          const uint32_t word = (uint32_t)vb[g][c][bsel >> 2];
+          const int sh = 8 * (bsel & 3);
+          vb[g][c][bsel >> 2] = (int)((word & ~(0xffu << sh)) | (code << sh));
+        }
+      }
+  }
 
   // ---- PV ------------------------------------------------------------------------
   float o[NCW][4];
@@ -395,8 +496,12 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   dim3 mgrid((unsigned)a.num_q_heads, (unsigned)a.num_seqs, (unsigned)(a.head_dim / 64));
 #define I8KV_DECODE_CASE(DD, GG)                                                             \
   if (a.head_dim == DD && a.w_group == GG) {                                                 \
-    hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG>), grid,                        \
-                       dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                     \
+    if (a.new_key)                                                                           \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true>), grid,                \
+                         dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
+    else                                                                                     \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false>), grid,               \
+                         dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
     if (a.max_parts > 1)                                                                     \
       hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(kWave), 0, stream, a); \
     return hipGetLastError();                                                                \

@@ -183,4 +183,66 @@ __device__ __forceinline__ float exp_f32_rn(float x) {
   return (float)__builtin_ldexp(p, (int)n);
 }
 
+// ---- one wave quantizes one D-vector of bf16 (the producer's rule) ---------
+// Lane l owns the D/64 consecutive elements l*D/64 ..; `raw` holds their bf16
+// bits (element i in bits 16i..16i+15).  Returns the lane's codes packed one
+// byte per element and sets `scale`: amax = max |x| over the wave, scale =
+// amax / 127 (IEEE), code = clamp(round(x / scale), -127, 127), and scale 0
+// with all-zero codes when amax = 0.
+template <int D>
+__device__ __forceinline__ uint32_t quantize_wave_vector(uint2 raw, float& scale) {
+  constexpr int EPL = D / kWave;
+  float x[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const uint32_t word = i < 2 ? raw.x : raw.y;
+    x[i] = bf16_bits_to_float((word >> (16 * (i & 1))) & 0xffffu);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = group_max<kWave>(amax);
+  float s = 0.0f;
+  uint32_t packed = 0;
+  if (amax != 0.0f) {
+    s = amax / 127.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) packed |= ((uint32_t)(quantize_code(x[i], s) & 0xff)) << (8 * i);
+  }
+  scale = s;
+  return packed;
+}
+
+// The lane's D/64 bf16 elements of a D-vector (see quantize_wave_vector).
+template <int D>
+__device__ __forceinline__ uint2 load_wave_vector(const uint16_t* src, int lane) {
+  constexpr int EPL = D / kWave;
+  if constexpr (EPL == 4) return *reinterpret_cast<const uint2*>(src + lane * 4);
+  else if constexpr (EPL == 2) return make_uint2(*reinterpret_cast<const uint32_t*>(src + lane * 2), 0u);
+  else return make_uint2((uint32_t)src[lane], 0u);
+}
+
+// Stores of one quantized token into the paged caches (lane's D/64 codes):
+// K [blk, h, d/16, off, d%16] -- the lane's bytes sit in one 16-byte chunk;
+// V [blk, h, d, off] -- one byte per (dim, token).
+template <int D>
+__device__ __forceinline__ void store_k_token(int8_t* k_cache, int64_t blk, int h, int Hkv, int off,
+                                              int lane, uint32_t packed) {
+  constexpr int EPL = D / kWave;
+  const int d0 = lane * EPL;
+  int8_t* dst = k_cache + (((blk * Hkv + h) * (D / 16) + d0 / 16) * kBlockSize + off) * 16 + d0 % 16;
+  if constexpr (EPL == 4) *reinterpret_cast<uint32_t*>(dst) = packed;
+  else if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+  else *dst = (int8_t)packed;
+}
+template <int D>
+__device__ __forceinline__ void store_v_token(int8_t* v_cache, int64_t blk, int h, int Hkv, int off,
+                                              int lane, uint32_t packed) {
+  constexpr int EPL = D / kWave;
+  const int d0 = lane * EPL;
+  int8_t* dst = v_cache + ((blk * Hkv + h) * D + d0) * kBlockSize + off;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) dst[i * kBlockSize] = (int8_t)(packed >> (8 * i));
+}
+
 }  // namespace i8kv

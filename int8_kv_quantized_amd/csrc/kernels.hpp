@@ -50,6 +50,17 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   float* out;
+  // fused step (producer of each sequence's newest token + decode); new_key is
+  // null for a plain decode
+  const uint16_t* new_key;    // [S, Hkv, D] bf16
+  const uint16_t* new_value;  // [S, Hkv, D] bf16
+  const uint16_t* new_query;  // [S, Hq, D] bf16
+  int8_t* k_cache_w;          // the caches, written at position seq_lens[s] - 1
+  int8_t* v_cache_w;
+  float* k_scale_w;
+  float* v_scale_w;
+  int8_t* q_int8_w;           // optional Q outputs [S, Hq, D], [S, Hq]
+  float* q_scale_w;
   // workspace views
   float* part_o;    // [S, Hkv, max_parts, group, D]
   float* part_ml;   // [S, Hkv, max_parts, group, 2]

@@ -48,33 +48,8 @@ __global__ __launch_bounds__(256) void kv_quantize_write_kernel(ProducerArgs a) 
     if (slot < 0 || (int64_t)slot >= (int64_t)a.num_blocks * kBlockSize) return;
   }
 
-  float x[EPL];
-  if constexpr (EPL == 4) {
-    const uint2 raw = *reinterpret_cast<const uint2*>(src + lane * 4);
-    x[0] = bf16_bits_to_float(raw.x & 0xffffu);
-    x[1] = bf16_bits_to_float(raw.x >> 16);
-    x[2] = bf16_bits_to_float(raw.y & 0xffffu);
-    x[3] = bf16_bits_to_float(raw.y >> 16);
-  } else if constexpr (EPL == 2) {
-    const uint32_t raw = *reinterpret_cast<const uint32_t*>(src + lane * 2);
-    x[0] = bf16_bits_to_float(raw & 0xffffu);
-    x[1] = bf16_bits_to_float(raw >> 16);
-  } else {
-    x[0] = bf16_bits_to_float(src[lane]);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  amax = group_max<kWave>(amax);
-
   float s = 0.0f;
-  uint32_t packed = 0;
-  if (amax != 0.0f) {
-    s = amax / 127.0f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      packed |= ((uint32_t)(quantize_code(x[i], s) & 0xff)) << (8 * i);
-  }
+  const uint32_t packed = quantize_wave_vector<D>(load_wave_vector<D>(src, lane), s);
 
   const int d0 = lane * EPL;
   if (kind == 2) {
@@ -89,19 +64,10 @@ __global__ __launch_bounds__(256) void kv_quantize_write_kernel(ProducerArgs a) 
   const int off = slot % kBlockSize;
   const int64_t sidx = (blk * kBlockSize + off) * a.num_kv_heads + h;
   if (kind == 0) {
-    // K [blk, h, d/16, off, d%16]: this lane's EPL bytes sit in one chunk.
-    int8_t* dst = a.k_cache +
-                  (((blk * a.num_kv_heads + h) * (D / 16) + d0 / 16) * kBlockSize + off) * 16 +
-                  d0 % 16;
-    if constexpr (EPL == 4) *reinterpret_cast<uint32_t*>(dst) = packed;
-    else if constexpr (EPL == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
-    else *dst = (int8_t)packed;
+    store_k_token<D>(a.k_cache, blk, h, a.num_kv_heads, off, lane, packed);
     if (lane == 0) a.k_scale[sidx] = s;
   } else {
-    // V [blk, h, d, off]: tokens innermost, one byte per (d, off).
-    int8_t* dst = a.v_cache + ((blk * a.num_kv_heads + h) * D + d0) * kBlockSize + off;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) dst[i * kBlockSize] = (int8_t)(packed >> (8 * i));
+    store_v_token<D>(a.v_cache, blk, h, a.num_kv_heads, off, lane, packed);
     if (lane == 0) a.v_scale[sidx] = s;
   }
 }

@@ -23,9 +23,10 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(i8kv_[a-z0-9_]+)\s*\(", text)))
 
 
-def test_header_declares_the_three_operations():
+def test_header_declares_the_operations():
     names = declared_functions()
-    for op in ("i8kv_kv_quantize_write", "i8kv_paged_decode_int8", "i8kv_prefix_prefill_int8"):
+    for op in ("i8kv_kv_quantize_write", "i8kv_paged_decode_int8", "i8kv_prefix_prefill_int8",
+               "i8kv_decode_step_int8"):
         assert op in names
 
 
@@ -118,6 +119,34 @@ def test_decode_workspace_query():
 ])
 def test_decode_validation(kw, expect):
     assert decode(desc(), **kw) == expect
+
+
+# --- fused decode step -----------------------------------------------------------
+def decode_step(d, S=2, key=FAKE, value=FAKE, query=FAKE, q8=None, qs=None, kc=FAKE, vc=FAKE,
+                ks=FAKE, vs=FAKE, bt=FAKE, max_blocks=32, sl=FAKE, max_len=512, part=256, G=32,
+                scale=0.0625, ws=FAKE, ws_bytes=1 << 30, out=FAKE):
+    P = lambda x: None if x is None else C.c_void_p(x)
+    return _lib().i8kv_decode_step_int8(
+        None if d is None else C.byref(d), S, P(key), P(value), P(query), P(q8), P(qs), P(kc),
+        P(vc), P(ks), P(vs), P(bt), max_blocks, P(sl), max_len, part, G, scale, P(ws), ws_bytes,
+        P(out), None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(key=None), NULL), (dict(value=None), NULL), (dict(query=None), NULL),
+    (dict(q8=FAKE), NULL), (dict(qs=FAKE), NULL), (dict(kc=None), NULL), (dict(out=None), NULL),
+    (dict(key=FAKE + 2), INVALID), (dict(q8=FAKE + 4, qs=FAKE), INVALID),
+    (dict(S=-1), INVALID), (dict(max_len=16 * 32 + 1), INVALID), (dict(G=16), UNSUPPORTED),
+    (dict(part=128), UNSUPPORTED), (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+    (dict(S=0), OK), (dict(S=0, q8=FAKE, qs=FAKE), OK),
+])
+def test_decode_step_validation(kw, expect):
+    assert decode_step(desc(), **kw) == expect
+
+
+def test_decode_step_descriptor_checked_first():
+    assert decode_step(None) == NULL
+    assert decode_step(desc(D=96)) == UNSUPPORTED
 
 
 # --- prefill ------------------------------------------------------------------
