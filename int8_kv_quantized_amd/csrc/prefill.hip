@@ -167,25 +167,35 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
   // Wave w copies pieces w, w + kNW, ... of the 2 * NPC 1 KiB pieces of a tile
   // (K pieces first, then V); the last two waves also copy the 64 K and V
   // scales.  Lane l of a K piece fetches the key that belongs at slot l & 15.
+  // The pieces a wave copies are the same for every tile: their page in the
+  // tile, LDS offset and per-lane source offset are set up once (wave-uniform
+  // except the lane offset); per tile only the page id changes.
+  constexpr int kMaxPieces = (2 * NPC + kNW - 1) / kNW;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int koff_lane = (lane >> 4) * 256 + kperm(lane & 15) * 16;
+  int pc_j[kMaxPieces], pc_lds[kMaxPieces], pc_src[kMaxPieces];
+  bool pc_v[kMaxPieces];
+#pragma unroll
+  for (int i = 0; i < kMaxPieces; ++i) {
+    const int q = min(wu + i * kNW, 2 * NPC - 1);
+    pc_v[i] = q >= NPC;
+    const int qq = pc_v[i] ? q - NPC : q;
+    const int cp = qq % PPP;
+    pc_j[i] = qq / PPP;
+    pc_lds[i] = pc_v[i] ? pc_j[i] * D * 16 + cp * 1024 : pc_j[i] * (D * 16 + 128) + cp * 1024;
+    pc_src[i] = cp * 1024 + (pc_v[i] ? lane * 16 : koff_lane);
+  }
   auto issue_tile = [&](int t, int buf) {
     const int k0 = t * kKT;
-    for (int q = w; q < 2 * NPC; q += kNW) {  // wave-uniform
-      const bool isv = q >= NPC;
-      const int qq = isv ? q - NPC : q;
-      const int j = qq / PPP, cp = qq % PPP;
-      const int pid = __builtin_amdgcn_readfirstlane(page_id(k0 / kBlockSize + j));
-      const size_t page = ((size_t)pid * Hkv + kv) * (size_t)D * 16 + (size_t)cp * 1024;
-      if (isv)
-        __builtin_amdgcn_global_load_lds(a.v_cache + page + lane * 16,
-                                         (__attribute__((address_space(3))) void*)
-                                             (s_v[buf] + j * D * 16 + cp * 1024),
-                                         16, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds(a.k_cache + page + koff_lane,
-                                         (__attribute__((address_space(3))) void*)
-                                             (s_k[buf] + j * (D * 16 + 128) + cp * 1024),
-                                         16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kMaxPieces; ++i) {
+      if (wu + i * kNW >= 2 * NPC) break;  // wave-uniform
+      const int pid = __builtin_amdgcn_readfirstlane(page_id(k0 / kBlockSize + pc_j[i]));
+      const int8_t* src = (pc_v[i] ? a.v_cache : a.k_cache) +
+                          ((size_t)pid * Hkv + kv) * (size_t)D * 16 + pc_src[i];
+      int8_t* dst = (pc_v[i] ? s_v[buf] : s_k[buf]) + pc_lds[i];
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0,
+                                       0);
     }
     if (w >= kNW - 2) {  // scale of key k0 + lane (keys past the sequence: any finite
                          // or not value, discarded by the masked path)
