@@ -58,6 +58,8 @@ class Oracle:
         L.orc_quantize_w.restype = None
         L.orc_quantize_w.argtypes = [_P, _I, _P, _P]
         L.orc_kv_quantize_write.argtypes = [_I] * 6 + [_P] * 10
+        L.orc_kv_quantize_write_rope.argtypes = [_I] * 6 + [_P] * 8 + [_I, _I] + [_P] * 4
+        L.orc_rope_rotate.argtypes = [_I, _I, _P, _P, _P, _I, _I]
         L.orc_paged_decode.argtypes = ([_I] * 6 + [_P] * 7 + [_I, _P, _I, _I, _F, _I, _P])
         L.orc_decode_head.argtypes = ([_I] * 7 + [_P] * 7 + [_I, _P, _I, _I, _F, _I,
                                                               C.POINTER(_DecodeTrace), _P])
@@ -112,6 +114,42 @@ class Oracle:
         if rc:
             raise ValueError(f"orc_kv_quantize_write rejected its arguments ({rc})")
         return q_int8, q_scale
+
+    def kv_quantize_write_rope(self, key, value, slot_mapping, positions, cos_sin, cache, *,
+                               num_q_heads, query=None):
+        """The producer with RoPE on Q and K (rotate-half pairing over the
+        first cos_sin.shape[1] dims, cos_sin [max_position, R] = cos | sin)."""
+        key = _c(key, np.uint16)
+        value = _c(value, np.uint16)
+        slot = _c(slot_mapping, np.int32)
+        pos = _c(positions, np.int32)
+        cs = _c(cos_sin, np.float32)
+        T, Hkv, D = key.shape
+        nb, _, _, bs, _ = cache["k_cache"].shape
+        q_int8 = q_scale = None
+        if query is not None:
+            query = _c(query, np.uint16)
+            q_int8 = np.zeros(query.shape, np.int8)
+            q_scale = np.zeros(query.shape[:2], np.float32)
+        rc = self.lib.orc_kv_quantize_write_rope(
+            T, num_q_heads, Hkv, D, bs, nb, _ptr(key), _ptr(value), _ptr(query),
+            _ptr(q_int8), _ptr(q_scale), _ptr(slot), _ptr(pos), _ptr(cs), cs.shape[1],
+            cs.shape[0], _ptr(cache["k_cache"]), _ptr(cache["v_cache"]),
+            _ptr(cache["k_scale"]), _ptr(cache["v_scale"]))
+        if rc:
+            raise ValueError(f"orc_kv_quantize_write_rope rejected its arguments ({rc})")
+        return q_int8, q_scale
+
+    def rope_rotate(self, x, positions, cos_sin):
+        """The rotation alone: x [n, D] fp32 (a rotated copy is returned)."""
+        x = _c(x, np.float32).copy()
+        pos = _c(positions, np.int32)
+        cs = _c(cos_sin, np.float32)
+        rc = self.lib.orc_rope_rotate(x.shape[0], x.shape[1], _ptr(x), _ptr(pos), _ptr(cs),
+                                      cs.shape[1], cs.shape[0])
+        if rc:
+            raise ValueError(f"orc_rope_rotate rejected its arguments ({rc})")
+        return x
 
     def fill(self, wl):
         """Write every cache token of a workload; quantize its query tokens.

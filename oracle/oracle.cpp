@@ -20,6 +20,9 @@
  *  - q head h reads KV head h / (Hq / Hkv);
  *  - the score is ((acc * sQ) * sK) * softmax_scale, left to right in fp32;
  *  - partitions are merged with weights l_p * exp(m_p - M), M = max m_p.
+ *  - RoPE, where the producer applies it, is the rotate-half pairing over
+ *    the first R dims with a caller-given cos|sin table per position, each
+ *    product and the sum / difference rounded to fp32; V is not rotated.
  *
  * Parity pins: see the oracle tests (worked quantization example, brute force
  * against unquantized fp64 attention with an a-priori bound, partition/tile
@@ -163,22 +166,44 @@ void orc_quantize_w(const float* w, int n, int8_t* wq, float* sw) {
   orc_quantize(w, n, wq, sw);
 }
 
-int orc_kv_quantize_write(int T, int Hq, int Hkv, int D, int bs, int nb,
-                          const uint16_t* key, const uint16_t* value,
-                          const uint16_t* query, int8_t* q_int8, float* q_scale,
-                          const int32_t* slot_mapping, int8_t* k_cache,
-                          int8_t* v_cache, float* k_scale, float* v_scale) {
+/* [KV 2.2] step 2, in the reading documented in oracle.h: the rotate-half
+ * pairing (j, j + R/2) for j < R/2, turned by the tabulated cosine / sine of
+ * the token's position; each product and the difference / sum rounded to
+ * fp32 on its own (no fused multiply-add). */
+static void rope_rotate(float* x, int R, const float* cs /* [R]: cos, then sin */) {
+  const int h = R / 2;
+  for (int j = 0; j < h; ++j) {
+    const float x1 = x[j], x2 = x[j + h], c = cs[j], s = cs[h + j];
+    const float a = x1 * c, b = x2 * s, e = x2 * c, f = x1 * s;
+    x[j] = a - b;
+    x[j + h] = e + f;
+  }
+}
+
+static int kv_quantize_write_impl(int T, int Hq, int Hkv, int D, int bs, int nb,
+                                  const uint16_t* key, const uint16_t* value,
+                                  const uint16_t* query, int8_t* q_int8, float* q_scale,
+                                  const int32_t* slot_mapping, const int32_t* positions,
+                                  const float* cos_sin, int R, int max_position,
+                                  int8_t* k_cache, int8_t* v_cache, float* k_scale,
+                                  float* v_scale) {
   if (T < 0 || !geometry_ok(Hq, Hkv, D, bs, nb)) return -1;
   if (query && (!q_int8 || !q_scale)) return -1;
+  if (positions && (!cos_sin || R < 2 || R > D || R % 2 || max_position <= 0)) return -1;
+  for (int t = 0; positions && t < T; ++t)
+    if (positions[t] < 0 || positions[t] >= max_position) return -3;
   Cache c{Hq, Hkv, D, bs, nb, k_cache, v_cache, k_scale, v_scale};
   std::vector<float> x(D);
   std::vector<int8_t> q(D);
   for (int t = 0; t < T; ++t) {
-    /* Query: quantized once per (token, q head) and kept for reuse [KV 2.2]. */
+    const float* cs = positions ? cos_sin + (size_t)positions[t] * R : nullptr;
+    /* Query: rotated, then quantized once per (token, q head) and kept for
+     * reuse [KV 2.2]. */
     if (query) {
       for (int h = 0; h < Hq; ++h) {
         const uint16_t* src = query + ((size_t)t * Hq + h) * D;
         for (int d = 0; d < D; ++d) x[d] = bf16_to_float(src[d]);
+        if (cs) rope_rotate(x.data(), R, cs);
         orc_quantize(x.data(), D, q_int8 + ((size_t)t * Hq + h) * D,
                      q_scale + (size_t)t * Hq + h);
       }
@@ -191,6 +216,7 @@ int orc_kv_quantize_write(int T, int Hq, int Hkv, int D, int bs, int nb,
       float s = 0.0f;
       const uint16_t* ks = key + ((size_t)t * Hkv + h) * D;
       for (int d = 0; d < D; ++d) x[d] = bf16_to_float(ks[d]);
+      if (cs) rope_rotate(x.data(), R, cs);
       orc_quantize(x.data(), D, q.data(), &s);
       for (int d = 0; d < D; ++d) k_cache[c.k_index(blk, h, off, d)] = q[d];
       k_scale[c.s_index(blk, h, off)] = s;
@@ -201,6 +227,40 @@ int orc_kv_quantize_write(int T, int Hq, int Hkv, int D, int bs, int nb,
       for (int d = 0; d < D; ++d) v_cache[c.v_index(blk, h, off, d)] = q[d];
       v_scale[c.s_index(blk, h, off)] = s;
     }
+  }
+  return 0;
+}
+
+int orc_kv_quantize_write(int T, int Hq, int Hkv, int D, int bs, int nb,
+                          const uint16_t* key, const uint16_t* value,
+                          const uint16_t* query, int8_t* q_int8, float* q_scale,
+                          const int32_t* slot_mapping, int8_t* k_cache,
+                          int8_t* v_cache, float* k_scale, float* v_scale) {
+  return kv_quantize_write_impl(T, Hq, Hkv, D, bs, nb, key, value, query, q_int8, q_scale,
+                                slot_mapping, nullptr, nullptr, 0, 0, k_cache, v_cache, k_scale,
+                                v_scale);
+}
+
+int orc_kv_quantize_write_rope(int T, int Hq, int Hkv, int D, int bs, int nb,
+                               const uint16_t* key, const uint16_t* value,
+                               const uint16_t* query, int8_t* q_int8, float* q_scale,
+                               const int32_t* slot_mapping, const int32_t* positions,
+                               const float* cos_sin, int rotary_dim, int max_position,
+                               int8_t* k_cache, int8_t* v_cache, float* k_scale,
+                               float* v_scale) {
+  if (!positions) return -1;
+  return kv_quantize_write_impl(T, Hq, Hkv, D, bs, nb, key, value, query, q_int8, q_scale,
+                                slot_mapping, positions, cos_sin, rotary_dim, max_position,
+                                k_cache, v_cache, k_scale, v_scale);
+}
+
+/* The rotation alone (for the pins): x [n, D] fp32 in place, pos [n]. */
+int orc_rope_rotate(int n, int D, float* x, const int32_t* positions, const float* cos_sin,
+                    int rotary_dim, int max_position) {
+  if (n < 0 || rotary_dim < 2 || rotary_dim > D || rotary_dim % 2) return -1;
+  for (int i = 0; i < n; ++i) {
+    if (positions[i] < 0 || positions[i] >= max_position) return -3;
+    rope_rotate(x + (size_t)i * D, rotary_dim, cos_sin + (size_t)positions[i] * rotary_dim);
   }
   return 0;
 }

@@ -64,6 +64,30 @@ int orc_kv_quantize_write(int T, int Hq, int Hkv, int D, int bs, int nb,
                           const int32_t* slot_mapping, int8_t* k_cache,
                           int8_t* v_cache, float* k_scale, float* v_scale);
 
+/* Producer with rotary position embedding of Q and K before quantization
+ * ([KV 2.2] step 2).  The pages name the step but not its variant; the
+ * reading taken is the rotate-half pairing over the first R = rotary_dim
+ * dims: for j < R/2 the pair (x[j], x[j + R/2]) turns by the angle whose
+ * cosine and sine the caller tabulates per position,
+ *   c = cos_sin[pos][j], s = cos_sin[pos][R/2 + j],
+ *   x'[j] = x[j] c - x[j + R/2] s,  x'[j + R/2] = x[j + R/2] c + x[j] s,
+ * each product and the difference / sum rounded to fp32 on its own (no fused
+ * multiply-add); dims R..D-1 pass unchanged.  V is not rotated.
+ *   positions [T] int32 in [0, max_position) (else -3)
+ *   cos_sin [max_position, R] fp32 */
+int orc_kv_quantize_write_rope(int T, int Hq, int Hkv, int D, int bs, int nb,
+                               const uint16_t* key, const uint16_t* value,
+                               const uint16_t* query, int8_t* q_int8, float* q_scale,
+                               const int32_t* slot_mapping, const int32_t* positions,
+                               const float* cos_sin, int rotary_dim, int max_position,
+                               int8_t* k_cache, int8_t* v_cache, float* k_scale,
+                               float* v_scale);
+
+/* The rotation of orc_kv_quantize_write_rope alone, in place on n fp32
+ * vectors of D values (x [n, D]) at positions [n]. */
+int orc_rope_rotate(int n, int D, float* x, const int32_t* positions, const float* cos_sin,
+                    int rotary_dim, int max_position);
+
 /* Per-(seq, q head) record of the decode computation. All pointers may be
  * NULL. L = seq_len, NP = ceil(L/partition), NG = number of W groups. */
 typedef struct {

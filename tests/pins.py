@@ -19,6 +19,10 @@ when the oracle disagrees with what the pages or the mathematics fix:
 * brute force against unquantized fp64 attention within an a-priori bound;
 * special cases with closed-form answers (one token, equal scores, one
   dominant score, empty sequence).
+* the rotary embedding against complex multiplication in fp64 (within the
+  rounding of two fp32 products and a sum), exact quarter turns and identity
+  tables, relative-position invariance of dot products; the producer with
+  RoPE against nearest codes of the fp64-rotated vectors.
 
 The mutation tests run the same functions on oracle builds with planted
 mistakes and require at least one pin to fail for each.
@@ -165,6 +169,131 @@ def pin_cache_layout(orc):
             assert sK[slots[t], h] == ks and sV[slots[t], h] == vs, "scale layout"
     assert not K[~written].any() and not V[~written].any(), "write outside its slot"
     assert not sK[~written].any() and not sV[~written].any(), "scale write outside its slot"
+
+
+# ---------------------------------------------------------------------------
+# rotary position embedding in the producer
+# ---------------------------------------------------------------------------
+U32 = 2.0 ** -24     # unit roundoff of fp32
+
+
+def _rotate_complex(x, pos, cs):
+    """fp64 reference: the first R dims as R/2 complex numbers
+    z_j = x[j] + i x[j + R/2], each multiplied by c + i s from the table
+    (the rotate-half pairing); returns (rotated, per-element error bound of a
+    product/product/difference evaluation in fp32)."""
+    x = np.asarray(x, np.float64)
+    R = cs.shape[1]
+    h = R // 2
+    c = cs[pos, :h].astype(np.float64)
+    s = cs[pos, h:].astype(np.float64)
+    z = (x[:, :h] + 1j * x[:, h:R]) * (c + 1j * s)
+    out = x.copy()
+    out[:, :h], out[:, h:R] = z.real, z.imag
+    mag = np.abs(x[:, :h] * c) + np.abs(x[:, h:R] * s)
+    mag2 = np.abs(x[:, h:R] * c) + np.abs(x[:, :h] * s)
+    bound = np.zeros_like(x)
+    bound[:, :h], bound[:, h:R] = 2.001 * U32 * mag, 2.001 * U32 * mag2
+    return out, bound
+
+
+def pin_rope_rotation(orc, seed=41):
+    """The rotation against complex multiplication in fp64 (within the fp32
+    rounding of two products and one sum), on random-angle and standard
+    tables, full and partial rotary dims; dims past R unchanged; the identity
+    table leaves every bit; relative-position invariance of dot products."""
+    rng = np.random.default_rng(seed)
+    for D, R in ((64, 64), (128, 64), (256, 256), (32, 8)):
+        for table in ("random", "standard"):
+            P = 300
+            cs = (W.random_cos_sin(rng, P, R) if table == "random"
+                  else W.rope_cos_sin(P, R))
+            x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(
+                rng.standard_normal((40, D), dtype=np.float32)))
+            pos = rng.integers(0, P, 40).astype(np.int32)
+            got = orc.rope_rotate(x, pos, cs)
+            ref, bound = _rotate_complex(x, pos, cs)
+            err = np.abs(got.astype(np.float64) - ref)
+            assert np.all(err <= bound), \
+                f"rotation (D={D}, R={R}, {table}) off by {float((err - bound).max())}"
+            assert np.array_equal(got[:, R:], x[:, R:]), "dims past the rotary part changed"
+    # identity table: cos 1, sin 0
+    x = rng.standard_normal((8, 128), dtype=np.float32)
+    cs = np.concatenate([np.ones((5, 32), np.float32), np.zeros((5, 32), np.float32)], 1)
+    assert np.array_equal(orc.rope_rotate(x, np.arange(8, dtype=np.int32) % 5, cs), x)
+    # a quarter turn: cos 0, sin 1 maps (a, b) -> (-b, a) exactly
+    cs = np.concatenate([np.zeros((1, 32), np.float32), np.ones((1, 32), np.float32)], 1)
+    got = orc.rope_rotate(x, np.zeros(8, np.int32), cs)
+    assert np.array_equal(got[:, :32], -x[:, 32:64]) and np.array_equal(got[:, 32:64], x[:, :32])
+    # relative positions: <R_p q, R_n k> depends on p - n only
+    R, P = 128, 4096
+    cs = W.rope_cos_sin(P, R)
+    q = rng.standard_normal((1, R)).astype(np.float32)
+    k = rng.standard_normal((1, R)).astype(np.float32)
+    for p, n, shift in ((7, 3, 1000), (2000, 1, 2095), (50, 50, 9)):
+        d0 = float(orc.rope_rotate(q, np.array([p], np.int32), cs)[0].astype(np.float64)
+                   @ orc.rope_rotate(k, np.array([n], np.int32), cs)[0])
+        d1 = float(orc.rope_rotate(q, np.array([p + shift], np.int32), cs)[0].astype(np.float64)
+                   @ orc.rope_rotate(k, np.array([n + shift], np.int32), cs)[0])
+        assert abs(d0 - d1) <= 2e-3 * (1 + abs(d0)), f"relative position ({p},{n}) {d0} vs {d1}"
+    # out-of-range positions are rejected
+    try:
+        orc.rope_rotate(x, np.full(8, 5, np.int32), cs[:5])
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("position past the table accepted")
+
+
+def pin_rope_producer(orc, seed=43):
+    """The producer with RoPE: Q and K codes are the nearest codes of the
+    rotated (fp64 complex reference) vectors within the fp32 rounding of the
+    rotation; V and the slots are those of the plain producer; an identity
+    table reproduces the plain producer bit for bit."""
+    rng = np.random.default_rng(seed)
+    for D, R in ((64, 64), (128, 32)):
+        wl = W.make_workload("rope", seq_lens=[37, 16, 1, 70], new_tokens=[1] * 4,
+                             num_q_heads=4, num_kv_heads=2, head_dim=D, seed=seed + D)
+        T = wl.num_tokens
+        qry = W.f32_to_bf16_bits(rng.standard_normal((T, 4, D), dtype=np.float32))
+        P = 128
+        cs = W.random_cos_sin(rng, P, R)
+        pos = rng.integers(0, P, T).astype(np.int32)
+        plain = orc.empty_cache(wl.num_blocks, 2, D)
+        q8p, qsp = orc.kv_quantize_write(wl.key, wl.value, wl.slot_mapping, plain,
+                                         num_q_heads=4, query=qry)
+        cache = orc.empty_cache(wl.num_blocks, 2, D)
+        q8, qs = orc.kv_quantize_write_rope(wl.key, wl.value, wl.slot_mapping, pos, cs, cache,
+                                            num_q_heads=4, query=qry)
+        for name in ("v_cache", "v_scale"):
+            assert np.array_equal(cache[name], plain[name]), f"{name} must not be rotated"
+        K, _, sK, _ = cache_rows(cache)
+        for t in range(T):
+            for h, (codes, sc, src) in enumerate(
+                    [(q8[t, j], qs[t, j], qry[t, j]) for j in range(4)]
+                    + [(K[wl.slot_mapping[t], j], sK[wl.slot_mapping[t], j], wl.key[t, j])
+                       for j in range(2)]):
+                x = W.bf16_bits_to_f32(src)[None]
+                ref, bound = _rotate_complex(x, pos[t:t + 1], cs)
+                ref, bound = ref[0], bound[0]
+                amax = np.abs(ref).max()
+                exp_s = amax / 127
+                assert abs(float(sc) - exp_s) <= 1e-6 * exp_s + bound.max() / 127, \
+                    f"scale of token {t} vector {h}"
+                # the code is the nearest one, up to a tie the rotation's rounding may decide
+                r = ref / np.float64(sc)
+                slack = bound / np.float64(sc) + 2e-6 * np.abs(r) + 1e-9
+                assert np.all(np.abs(codes.astype(np.float64) - r) <= 0.5 + slack), \
+                    f"code of token {t} vector {h} not nearest to the rotated value"
+        # identity table == plain producer
+        ident = np.concatenate([np.ones((P, R // 2), np.float32),
+                                np.zeros((P, R // 2), np.float32)], 1)
+        cache_i = orc.empty_cache(wl.num_blocks, 2, D)
+        q8i, qsi = orc.kv_quantize_write_rope(wl.key, wl.value, wl.slot_mapping, pos, ident,
+                                              cache_i, num_q_heads=4, query=qry)
+        assert np.array_equal(q8i, q8p) and np.array_equal(qsi, qsp), "identity table, Q"
+        for name in plain:
+            assert np.array_equal(cache_i[name], plain[name]), f"identity table, {name}"
 
 
 # ---------------------------------------------------------------------------
@@ -472,4 +601,4 @@ def pin_prefill_vs_decode(orc, G=32, seed=9):
 ALL_PINS = [pin_quantize_golden, pin_quantize_bruteforce, pin_cache_layout,
             pin_decode_trace, pin_decode_bruteforce, pin_decode_partition_invariance,
             pin_decode_special_cases, pin_prefill_exact, pin_prefill_trace,
-            pin_prefill_vs_decode]
+            pin_prefill_vs_decode, pin_rope_rotation, pin_rope_producer]

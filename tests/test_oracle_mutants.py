@@ -60,6 +60,33 @@ MUTANTS = {
     "prefill_not_causal": [("const int pos = ctx + (row - query_start_loc[b]);",
                             "const int pos = seq_lens[b] - 1;")],
     "prefill_excludes_self": [("const int nk = pos + 1;", "const int nk = pos > 0 ? pos : 1;")],
+    "rope_inverse_turn": [("    x[j] = a - b;\n    x[j + h] = e + f;",
+                           "    x[j] = a + b;\n    x[j + h] = e - f;")],
+    "rope_cos_sin_swapped": [("c = cs[j], s = cs[h + j];", "c = cs[h + j], s = cs[j];")],
+    "rope_interleaved_pairs": [(
+        "    const float x1 = x[j], x2 = x[j + h], c = cs[j], s = cs[h + j];\n"
+        "    const float a = x1 * c, b = x2 * s, e = x2 * c, f = x1 * s;\n"
+        "    x[j] = a - b;\n"
+        "    x[j + h] = e + f;",
+        "    const float x1 = x[2 * j], x2 = x[2 * j + 1], c = cs[j], s = cs[h + j];\n"
+        "    const float a = x1 * c, b = x2 * s, e = x2 * c, f = x1 * s;\n"
+        "    x[2 * j] = a - b;\n"
+        "    x[2 * j + 1] = e + f;")],
+    "rope_half_dims": [("  const int h = R / 2;\n  for (int j = 0; j < h; ++j) {",
+                        "  const int h = R / 2;\n  for (int j = 0; j < h / 2; ++j) {")],
+    "rope_skips_query": [("x[d] = bf16_to_float(src[d]);\n        if (cs) rope_rotate(x.data(), R, cs);",
+                          "x[d] = bf16_to_float(src[d]);")],
+    "rope_rotates_value": [("x[d] = bf16_to_float(vs[d]);\n",
+                            "x[d] = bf16_to_float(vs[d]);\n      if (cs) rope_rotate(x.data(), R, cs);\n")],
+    "rope_position_off_by_one": [("cos_sin + (size_t)positions[t] * R",
+                                  "cos_sin + (size_t)(positions[t] > 0 ? positions[t] - 1 : 1) * R")],
+    "rope_after_quantize": [(
+        "      if (cs) rope_rotate(x.data(), R, cs);\n      orc_quantize(x.data(), D, q.data(), &s);\n"
+        "      for (int d = 0; d < D; ++d) k_cache",
+        "      orc_quantize(x.data(), D, q.data(), &s);\n"
+        "      if (cs) { for (int d = 0; d < D; ++d) x[d] = q[d]; rope_rotate(x.data(), R, cs);\n"
+        "        for (int d = 0; d < D; ++d) q[d] = (int8_t)std::max(-127.0f, std::min(127.0f, std::round(x[d]))); }\n"
+        "      for (int d = 0; d < D; ++d) k_cache")],
 }
 
 

@@ -280,3 +280,27 @@ CONFIG_BUILDERS: Dict[str, object] = {
     "prefill_2048_over_16384": lambda G=32: cfg4_prefill(w_group=G),
     "mha_producer_decode": cfg5_mha_producer_decode,
 }
+
+
+# --------------------------------------------------------------------------
+# Rotary tables (an input of the producer, like the activations)
+# --------------------------------------------------------------------------
+def rope_cos_sin(max_position: int, rotary_dim: int, base: float = 10000.0) -> np.ndarray:
+    """The usual rotary table: angle(p, j) = p * base^(-2j/R) for j < R/2.
+
+    Returns fp32 ``[max_position, R]``: cosines in the first R/2 columns,
+    sines in the last R/2, each computed in fp64 and rounded once.
+    """
+    assert rotary_dim % 2 == 0 and rotary_dim >= 2
+    h = rotary_dim // 2
+    inv_freq = base ** (-2.0 * np.arange(h, dtype=np.float64) / rotary_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * inv_freq[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def random_cos_sin(rng: np.random.Generator, max_position: int,
+                   rotary_dim: int) -> np.ndarray:
+    """A table of uniformly random angles (every quadrant), same layout."""
+    h = rotary_dim // 2
+    ang = rng.uniform(-np.pi, np.pi, (max_position, h))
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
