@@ -10,7 +10,9 @@ workload is decode at 16384 tokens of history (batch 1, 24 q / 4 KV heads,
 head_dim 256, page 16, 1% of V channels x20, W group 32), with inputs
 resident in HBM and rotated over enough distinct cache copies (>= 512 MB) to
 defeat the 256 MB last-level cache.  The chunked-prefill path (2048 queries
-over 16384 cached tokens) is timed as well and reported as int8 TOPS.
+over 16384 cached tokens) is timed as well and reported as int8 TOPS, and so
+is the producer alone over 2242- and 4096-token chunks, with and without the
+rotary embedding fused in.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -49,6 +51,8 @@ def parse_args():
     p.add_argument("--min-rotation-mb", type=float, default=512.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-producer-chunks", action="store_true",
+                   help="skip the producer-alone timing over 2242- and 4096-token chunks")
     p.add_argument("--prefill-reps", type=int, default=10)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--sweep", action="store_true",
@@ -230,6 +234,68 @@ def time_prefill(reps, G=32, graph=True):
     return dict(us=us, ops=ops, tops=ops / (us * 1e-6) / 1e12, workload=wl.name)
 
 
+def time_producer_chunk(tokens, steps=50, min_rotation_mb=512.0):
+    """The producer alone over a prefill chunk of `tokens` tokens (24 q / 4 KV
+    heads, head_dim 256, every token with its query), without and with the
+    rotary embedding fused in; inputs and caches rotated over enough copies
+    to exceed the last-level cache.  Returns us per call and HBM GB/s of the
+    algorithmic bytes (bf16 Q/K/V read, int8 codes and fp32 scales written,
+    slot / position / table row read)."""
+    import numpy as np
+    import torch
+
+    import int8_kv_quantized_amd as K
+    import workloads as W
+    wl = W.producer_chunk(tokens)
+    d = K.CacheDesc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    Hq, Hkv, D, T = wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_tokens
+    R = D
+    per_tok = 2 * (Hq + 2 * Hkv) * D + (Hq + 2 * Hkv) * D + 4 * (Hq + 2 * Hkv) + 4
+    set_bytes = T * per_tok
+    copies = max(1, math.ceil(min_rotation_mb * 1e6 / set_bytes))
+    k0, v0, q0 = dev(wl.key), dev(wl.value), dev(wl.query)
+    sets = [(k0, v0, q0)] + [(k0.clone(), v0.clone(), q0.clone()) for _ in range(copies - 1)]
+    caches = [K.PagedCache.allocate(d) for _ in range(copies)]
+    slot, pos = dev(wl.slot_mapping), dev(wl.token_pos)
+    cs = dev(W.rope_cos_sin(T, R))
+    q8 = [torch.empty((T, Hq, D), dtype=torch.int8, device="cuda") for _ in range(copies)]
+    qs = [torch.empty((T, Hq), dtype=torch.float32, device="cuda") for _ in range(copies)]
+
+    def plain(i):
+        k, v, q = sets[i % copies]
+        K.kv_quantize_write(d, k, v, slot, caches[i % copies], query=q, q_int8=q8[i % copies],
+                            q_scale=qs[i % copies])
+
+    def rope(i):
+        k, v, q = sets[i % copies]
+        K.kv_quantize_write_rope(d, k, v, slot, pos, cs, caches[i % copies], query=q,
+                                 q_int8=q8[i % copies], q_scale=qs[i % copies])
+
+    res = {}
+    for name, fn, extra_b in (("plain", plain, 0), ("rope", rope, 4 + 4 * R)):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / steps
+        b = T * (per_tok + extra_b)
+        res[f"{name}_us"] = round(us, 3)
+        res[f"{name}_gbs"] = round(b / (us * 1e-6) / 1e9, 1)
+    res["bytes_plain"] = T * per_tok
+    return res
+
+
 DECODE_SOURCES = ["int8_kv_quantized_amd/csrc/decode.hip", "int8_kv_quantized_amd/csrc/kernels.hpp",
                   "int8_kv_quantized_amd/csrc/device_common.hpp"]
 
@@ -324,6 +390,12 @@ def main():
         extra.update(prefill_us=round(pf["us"], 2), prefill_int8_tops=round(pf["tops"], 2),
                      prefill_frac_of_int8_peak=round(pf["tops"] / INT8_PEAK_TOPS, 4),
                      prefill_ops=pf["ops"])
+    if not args.no_producer_chunks:
+        chunks = {}
+        for T in (2242, 4096):
+            chunks[f"T{T}"] = time_producer_chunk(T)
+            log(f"producer chunk T={T}: {chunks[f'T{T}']}")
+        extra["producer_chunk"] = chunks
     if args.sweep:
         sweep = {}
         for name in ["decode_L512", "decode_L4096", "decode_L8192", "decode_L16384",

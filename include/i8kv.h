@@ -1,13 +1,15 @@
 /*
  * i8kv -- paged attention over an INT8 KV cache, native to AMD MI355X (gfx950).
  *
- * C ABI of the library libi8kv.so.  Four calls, on the operations defined on the pages
+ * C ABI of the library libi8kv.so.  Five calls, on the operations defined on the pages
  *   [KV] "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
  *        DCU" (part 1 of the series), and
  *   [PV] "Implementing INT8 PV MMAC on a gfx936 DCU: V-scale fusion,
  *        probability quantization, fragment grouping" (part 3):
  *
  *   i8kv_kv_quantize_write  -- the fused KV producer ([KV] sections 2.1-2.3)
+ *   i8kv_kv_quantize_write_rope -- the same producer with the rotary
+ *                              embedding of Q and K fused in ([KV] 2.2)
  *   i8kv_paged_decode_int8  -- decode over 256-token partitions ([KV] 3.3,
  *                              [PV] 2.2, merge by log-sum-exp weights)
  *   i8kv_prefix_prefill_int8 -- chunked prefill with history in one online
@@ -94,6 +96,34 @@ i8kv_status i8kv_kv_quantize_write(const i8kv_cache_desc* desc, int32_t num_toke
                                    int8_t* k_cache, int8_t* v_cache,
                                    float* k_scale, float* v_scale,
                                    i8kv_stream_t stream);
+
+/*
+ * The fused KV producer with rotary position embedding ([KV] 2.2 lists RoPE
+ * as the producer's second step; the pages do not fix its variant).  Same as
+ * i8kv_kv_quantize_write, except that Q and K (not V) are first rotated by
+ * their token's position, in the rotate-half pairing over the first
+ * R = rotary_dim dims: for j < R/2, with c = cos_sin[pos][j] and
+ * s = cos_sin[pos][R/2 + j],
+ *   x[j]' = x[j] c - x[j + R/2] s,   x[j + R/2]' = x[j + R/2] c + x[j] s,
+ * each product and the difference / sum rounded to fp32 (no fused
+ * multiply-add); dims R..D-1 pass unchanged; the rotated fp32 vector is then
+ * quantized as above.
+ *   positions [T] int32, each in [0, max_position)
+ *   cos_sin   [max_position, R] fp32 (cosines, then sines), 4-byte aligned
+ * A position outside [0, max_position) is clamped into it on the device (no
+ * read leaves the table; the result for that token is then meaningless).
+ * Errors: as i8kv_kv_quantize_write; NULL for missing positions / cos_sin;
+ * INVALID_ARG for max_position <= 0, rotary_dim <= 0 or a misaligned table;
+ * UNSUPPORTED unless rotary_dim <= D and rotary_dim % (2 D / 64) == 0
+ * (even for D = 64, a multiple of 4 for D = 128 and of 8 for D = 256).
+ */
+i8kv_status i8kv_kv_quantize_write_rope(const i8kv_cache_desc* desc, int32_t num_tokens,
+                                        const uint16_t* key, const uint16_t* value,
+                                        const uint16_t* query, int8_t* q_int8, float* q_scale,
+                                        const int32_t* slot_mapping, const int32_t* positions,
+                                        const float* cos_sin, int32_t rotary_dim,
+                                        int32_t max_position, int8_t* k_cache, int8_t* v_cache,
+                                        float* k_scale, float* v_scale, i8kv_stream_t stream);
 
 /*
  * Bytes of device workspace that i8kv_paged_decode_int8 needs for num_seqs

@@ -7,6 +7,8 @@ host.  Importing it does not load the library; the first call does, and it
 fails loudly if the library has not been built -- there is no fallback.
 
     kv_quantize_write(desc, key, value, slot_mapping, cache, query=None, ...)
+    kv_quantize_write_rope(desc, key, value, slot_mapping, positions, cos_sin,
+                           cache, query=None, ...)
     paged_decode_workspace_bytes(desc, num_seqs, max_seq_len)
     paged_decode_int8(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
     prefix_prefill_int8(desc, q_int8, q_scale, query_start_loc, seq_lens,
@@ -20,6 +22,7 @@ from ._binding import (  # noqa: F401
     abi_version,
     decode_step_int8,
     kv_quantize_write,
+    kv_quantize_write_rope,
     lib_path,
     load_library,
     paged_decode_int8,

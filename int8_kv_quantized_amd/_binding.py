@@ -67,6 +67,8 @@ def load_library():
     lib.i8kv_status_string.argtypes = [C.c_int]
     lib.i8kv_kv_quantize_write.restype = C.c_int
     lib.i8kv_kv_quantize_write.argtypes = [D, I32] + [P] * 10 + [P]
+    lib.i8kv_kv_quantize_write_rope.restype = C.c_int
+    lib.i8kv_kv_quantize_write_rope.argtypes = [D, I32] + [P] * 8 + [I32, I32] + [P] * 4 + [P]
     lib.i8kv_paged_decode_workspace_bytes.restype = SZ
     lib.i8kv_paged_decode_workspace_bytes.argtypes = [D, I32, I32, I32]
     lib.i8kv_paged_decode_int8.restype = C.c_int
@@ -172,16 +174,9 @@ class PagedCache:
 # ---------------------------------------------------------------------------
 # the three operations
 # ---------------------------------------------------------------------------
-def kv_quantize_write(desc: CacheDesc, key, value, slot_mapping, cache: PagedCache,
-                      query=None, q_int8=None, q_scale=None, num_tokens: Optional[int] = None,
-                      stream=None):
-    """Fused producer: quantize K/V (and Q) and write the paged cache.
-
-    Returns ``(q_int8, q_scale)`` (allocated here when ``query`` is given and
-    they are not).
-    """
+def _producer_args(desc: CacheDesc, key, value, slot_mapping, cache: PagedCache, query,
+                   q_int8, q_scale, num_tokens):
     import torch
-    lib = load_library()
     if num_tokens is None:
         num_tokens = int(key.shape[0])
     T, Hq, Hkv, D = num_tokens, desc.num_q_heads, desc.num_kv_heads, desc.head_dim
@@ -203,11 +198,56 @@ def kv_quantize_write(desc: CacheDesc, key, value, slot_mapping, cache: PagedCac
             q_scale = torch.empty((T, Hq), dtype=torch.float32, device=key.device)
         _check(q_int8, "q_int8", torch.int8, (T, Hq, D))
         _check(q_scale, "q_scale", torch.float32, (T, Hq))
+    return T, q_int8, q_scale
+
+
+def kv_quantize_write(desc: CacheDesc, key, value, slot_mapping, cache: PagedCache,
+                      query=None, q_int8=None, q_scale=None, num_tokens: Optional[int] = None,
+                      stream=None):
+    """Fused producer: quantize K/V (and Q) and write the paged cache.
+
+    Returns ``(q_int8, q_scale)`` (allocated here when ``query`` is given and
+    they are not).
+    """
+    lib = load_library()
+    T, q_int8, q_scale = _producer_args(desc, key, value, slot_mapping, cache, query, q_int8,
+                                        q_scale, num_tokens)
     st = lib.i8kv_kv_quantize_write(
         C.byref(desc), T, _ptr(key), _ptr(value), _ptr(query), _ptr(q_int8), _ptr(q_scale),
         _ptr(slot_mapping), _ptr(cache.k_cache), _ptr(cache.v_cache), _ptr(cache.k_scale),
         _ptr(cache.v_scale), _stream(stream))
     _raise("kv_quantize_write", st)
+    return q_int8, q_scale
+
+
+def kv_quantize_write_rope(desc: CacheDesc, key, value, slot_mapping, positions, cos_sin,
+                           cache: PagedCache, query=None, q_int8=None, q_scale=None,
+                           num_tokens: Optional[int] = None, rotary_dim: Optional[int] = None,
+                           max_position: Optional[int] = None, stream=None):
+    """The producer with the rotary embedding of Q and K fused in.
+
+    ``positions`` [T] int32; ``cos_sin`` [max_position, rotary_dim] fp32
+    (cosines, then sines).  Returns ``(q_int8, q_scale)`` as kv_quantize_write.
+    """
+    import torch
+    lib = load_library()
+    T, q_int8, q_scale = _producer_args(desc, key, value, slot_mapping, cache, query, q_int8,
+                                        q_scale, num_tokens)
+    _check(positions, "positions", torch.int32, (T,))
+    _check(cos_sin, "cos_sin", torch.float32)
+    if _is_tensor(cos_sin):
+        if cos_sin.dim() != 2:
+            raise ValueError(f"cos_sin: shape {tuple(cos_sin.shape)}, expected (P, R)")
+        max_position = int(cos_sin.shape[0]) if max_position is None else max_position
+        rotary_dim = int(cos_sin.shape[1]) if rotary_dim is None else rotary_dim
+    if rotary_dim is None or max_position is None:
+        raise ValueError("rotary_dim and max_position are needed with a raw cos_sin pointer")
+    st = lib.i8kv_kv_quantize_write_rope(
+        C.byref(desc), T, _ptr(key), _ptr(value), _ptr(query), _ptr(q_int8), _ptr(q_scale),
+        _ptr(slot_mapping), _ptr(positions), _ptr(cos_sin), int(rotary_dim), int(max_position),
+        _ptr(cache.k_cache), _ptr(cache.v_cache), _ptr(cache.k_scale), _ptr(cache.v_scale),
+        _stream(stream))
+    _raise("kv_quantize_write_rope", st)
     return q_int8, q_scale
 
 

@@ -33,6 +33,53 @@ i8kv_status check_desc(const i8kv_cache_desc* d) {
 
 i8kv_status from_hip(hipError_t e) { return e == hipSuccess ? I8KV_OK : I8KV_ERR_LAUNCH; }
 
+// Shared by the producer entry points; positions == null means no rotation.
+i8kv_status run_producer(const i8kv_cache_desc* desc, int32_t num_tokens, const uint16_t* key,
+                         const uint16_t* value, const uint16_t* query, int8_t* q_int8,
+                         float* q_scale, const int32_t* slot_mapping, const int32_t* positions,
+                         const float* cos_sin, int32_t rotary_dim, int32_t max_position,
+                         int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
+                         i8kv_stream_t stream) {
+  i8kv_status st = check_desc(desc);
+  if (st != I8KV_OK) return st;
+  if (!key || !value || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+    return I8KV_ERR_NULL;
+  if (query && (!q_int8 || !q_scale)) return I8KV_ERR_NULL;
+  if (num_tokens < 0) return I8KV_ERR_INVALID_ARG;
+  if (!aligned16(key) || !aligned16(value) || (query && (!aligned16(query) || !aligned16(q_int8))) ||
+      !aligned16(k_cache) || !aligned16(v_cache))
+    return I8KV_ERR_INVALID_ARG;
+  if (positions) {
+    if (max_position <= 0 || rotary_dim <= 0 || (reinterpret_cast<uintptr_t>(cos_sin) & 3u))
+      return I8KV_ERR_INVALID_ARG;
+    const int per_lane = desc->head_dim / 64;
+    if (rotary_dim > desc->head_dim || rotary_dim % (2 * per_lane) != 0)
+      return I8KV_ERR_UNSUPPORTED;
+  }
+  if (num_tokens == 0) return I8KV_OK;
+  ProducerArgs a{};
+  a.num_tokens = num_tokens;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.head_dim = desc->head_dim;
+  a.num_blocks = desc->num_blocks;
+  a.key = key;
+  a.value = value;
+  a.query = query;
+  a.q_int8 = q_int8;
+  a.q_scale = q_scale;
+  a.slot_mapping = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.positions = positions;
+  a.cos_sin = cos_sin;
+  a.rotary_dim = rotary_dim;
+  a.max_position = max_position;
+  return from_hip(launch_kv_quantize_write(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -57,33 +104,21 @@ i8kv_status i8kv_kv_quantize_write(const i8kv_cache_desc* desc, int32_t num_toke
                                    const int32_t* slot_mapping, int8_t* k_cache,
                                    int8_t* v_cache, float* k_scale, float* v_scale,
                                    i8kv_stream_t stream) {
-  i8kv_status st = check_desc(desc);
-  if (st != I8KV_OK) return st;
-  if (!key || !value || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
-    return I8KV_ERR_NULL;
-  if (query && (!q_int8 || !q_scale)) return I8KV_ERR_NULL;
-  if (num_tokens < 0) return I8KV_ERR_INVALID_ARG;
-  if (!aligned16(key) || !aligned16(value) || (query && (!aligned16(query) || !aligned16(q_int8))) ||
-      !aligned16(k_cache) || !aligned16(v_cache))
-    return I8KV_ERR_INVALID_ARG;
-  if (num_tokens == 0) return I8KV_OK;
-  ProducerArgs a{};
-  a.num_tokens = num_tokens;
-  a.num_q_heads = desc->num_q_heads;
-  a.num_kv_heads = desc->num_kv_heads;
-  a.head_dim = desc->head_dim;
-  a.num_blocks = desc->num_blocks;
-  a.key = key;
-  a.value = value;
-  a.query = query;
-  a.q_int8 = q_int8;
-  a.q_scale = q_scale;
-  a.slot_mapping = slot_mapping;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  return from_hip(launch_kv_quantize_write(a, static_cast<hipStream_t>(stream)));
+  return run_producer(desc, num_tokens, key, value, query, q_int8, q_scale, slot_mapping,
+                      nullptr, nullptr, 0, 0, k_cache, v_cache, k_scale, v_scale, stream);
+}
+
+i8kv_status i8kv_kv_quantize_write_rope(const i8kv_cache_desc* desc, int32_t num_tokens,
+                                        const uint16_t* key, const uint16_t* value,
+                                        const uint16_t* query, int8_t* q_int8, float* q_scale,
+                                        const int32_t* slot_mapping, const int32_t* positions,
+                                        const float* cos_sin, int32_t rotary_dim,
+                                        int32_t max_position, int8_t* k_cache, int8_t* v_cache,
+                                        float* k_scale, float* v_scale, i8kv_stream_t stream) {
+  if (!positions || !cos_sin) return I8KV_ERR_NULL;
+  return run_producer(desc, num_tokens, key, value, query, q_int8, q_scale, slot_mapping,
+                      positions, cos_sin, rotary_dim, max_position, k_cache, v_cache, k_scale,
+                      v_scale, stream);
 }
 
 size_t i8kv_paged_decode_workspace_bytes(const i8kv_cache_desc* desc, int32_t num_seqs,

@@ -185,32 +185,182 @@ __device__ __forceinline__ float exp_f32_rn(float x) {
 
 // ---- one wave quantizes one D-vector of bf16 (the producer's rule) ---------
 // Lane l owns the D/64 consecutive elements l*D/64 ..; `raw` holds their bf16
-// bits (element i in bits 16i..16i+15).  Returns the lane's codes packed one
-// byte per element and sets `scale`: amax = max |x| over the wave, scale =
-// amax / 127 (IEEE), code = clamp(round(x / scale), -127, 127), and scale 0
-// with all-zero codes when amax = 0.
+// bits (element i in bits 16i..16i+15).
 template <int D>
-__device__ __forceinline__ uint32_t quantize_wave_vector(uint2 raw, float& scale) {
-  constexpr int EPL = D / kWave;
-  float x[EPL];
+__device__ __forceinline__ void unpack_wave_vector(uint2 raw, float (&x)[D / kWave]) {
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
+  for (int i = 0; i < D / kWave; ++i) {
     const uint32_t word = i < 2 ? raw.x : raw.y;
     x[i] = bf16_bits_to_float((word >> (16 * (i & 1))) & 0xffffu);
   }
+}
+
+// Returns the lane's codes packed one byte per element and sets `scale`:
+// amax = max |x| over the wave, scale = amax / 127 (IEEE), code =
+// clamp(round(x / scale), -127, 127), and scale 0 with all-zero codes when
+// amax = 0.
+// Codes of a lane's n elements given the vector's scale s (amax / 127) as
+//   sd = s, or 1 when amax = 0 (all elements are then zero), and rs = 1 / sd.
+// Fast rule: qh = fma(x, rs, 128.5 + 2^-14) lies within 1.9e-5 of the IEEE
+// quotient y = x / sd plus the same constant (|x| <= 127 sd, sd normal).  If
+// fract(qh) >= 2^-13, y + 128 is more than 1e-4 from every half-integer and
+// floor(qh) - 128 is the code clamp(round(y)) with ties away from zero (never
+// a tie, never outside [-127, 127]); the biased code (1..255) is converted
+// from the exact integer floor(qh) and the bias removed by flipping each
+// byte's top bit.  A lane with an element too close to a half-integer, or a
+// call with `divide` set (subnormal sd: 1 / sd may overflow), divides
+// instead.  (Checked on the CPU exhaustively for every bf16 x and amax with a
+// normal scale, and on random and near-midpoint fp32 inputs.)
+template <int n>
+__device__ __forceinline__ uint32_t quantize_codes_rs(const float (&x)[n], float sd, float rs,
+                                                      bool divide) {
+  static_assert(n >= 1 && n <= 4, "at most four codes per lane");
+  constexpr uint32_t kFlip = n == 4 ? 0x80808080u : n == 2 ? 0x8080u : 0x80u;
+  constexpr float kBias = 128.5f + 0x1p-14f;  // exact in fp32
+  float qh[n];
+  float fmin = 1.0f;
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    qh[i] = fmaf(x[i], rs, kBias);
+    fmin = fminf(fmin, __builtin_amdgcn_fractf(qh[i]));
+  }
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < n; ++i) packed = __builtin_amdgcn_cvt_pk_u8_f32(floorf(qh[i]), i, packed);
+  packed ^= kFlip;
+  if (divide || fmin < 0x1p-13f) {
+    packed = 0;
+#pragma unroll
+    for (int i = 0; i < n; ++i) packed |= ((uint32_t)(quantize_code(x[i], sd) & 0xff)) << (8 * i);
+  }
+  return packed;
+}
+
+// Returns the lane's codes packed one byte per element and sets `scale`:
+// amax = max |x| over the wave, scale = amax / 127 (IEEE), code =
+// clamp(round(x / scale), -127, 127), and scale 0 with all-zero codes when
+// amax = 0.
+// Codes of a lane's n elements given the vector's scale s (amax / 127) as
+//   sd = s, or 1 when amax = 0 (all elements are then zero), and rs = 1 / sd.
+// Fast rule: qb = fma(x, rs, 128) lies within 1.9e-5 of the IEEE quotient
+// x / sd plus 128 (|x| <= 127 sd, sd normal), so unless qb is within 2^-13 of
+// a rounding midpoint, rint(qb) - 128 is the code clamp(round(x / sd)) with
+// ties away from zero: it is never a tie and never outside [-127, 127].  The
+// biased code (1..255) is packed by the byte conversion and the bias removed
+// by flipping each byte's top bit.  A lane with an element near a midpoint,
+// or a subnormal sd (1 / sd may overflow), divides instead.  (Checked on the
+// CPU exhaustively for every bf16 x and amax with a normal scale, and on
+// random and near-midpoint fp32 inputs.)
+template <int n>
+__device__ __forceinline__ uint32_t quantize_codes_rs(const float (&x)[n], float sd, float rs) {
+  static_assert(n >= 1 && n <= 4, "at most four codes per lane");
+  constexpr uint32_t kBias = n == 4 ? 0x80808080u : n == 2 ? 0x8080u : 0x80u;
+  bool divide = !(sd >= 0x1p-126f);
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < n; ++i) {
+    const float qb = fmaf(x[i], rs, 128.0f);
+    const float c = rintf(qb);
+    divide |= fabsf(qb - c) > 0.5f - 0x1p-13f;
+    packed = __builtin_amdgcn_cvt_pk_u8_f32(c, i, packed);
+  }
+  packed ^= kBias;
+  if (divide) {
+    packed = 0;
+#pragma unroll
+    for (int i = 0; i < n; ++i) packed |= ((uint32_t)(quantize_code(x[i], sd) & 0xff)) << (8 * i);
+  }
+  return packed;
+}
+
+// Returns the lane's codes packed one byte per element and sets `scale`:
+// amax = max |x| over the wave, scale = amax / 127 (IEEE), code =
+// clamp(round(x / scale), -127, 127), and scale 0 with all-zero codes when
+// amax = 0.
+template <int D>
+__device__ __forceinline__ uint32_t quantize_wave_values(const float (&x)[D / kWave], float& scale) {
+  constexpr int EPL = D / kWave;
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) amax = fmaxf(amax, fabsf(x[i]));
   amax = group_max<kWave>(amax);
-  float s = 0.0f;
-  uint32_t packed = 0;
-  if (amax != 0.0f) {
-    s = amax / 127.0f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) packed |= ((uint32_t)(quantize_code(x[i], s) & 0xff)) << (8 * i);
-  }
+  const float s = amax / 127.0f;
+  const float sd = amax != 0.0f ? s : 1.0f;
   scale = s;
-  return packed;
+  return quantize_codes_rs<EPL>(x, sd, 1.0f / sd, !(sd >= 0x1p-126f));
+}
+
+// Wave maxima of 16 per-lane non-negative floats at once (a reduce-scatter,
+// on their bit patterns, whose unsigned order is the numeric order):
+// afterwards lane l holds the maximum over all 64 lanes of value l >> 2.
+// Each stage halves the values a lane keeps: v_permlane32_swap pairs the
+// wave's halves (lanes 0-31 keep values 0-7, lanes 32-63 values 8-15),
+// v_permlane16_swap pairs rows 2k and 2k+1, row_mirror pairs lane i with
+// 15 - i and row_half_mirror i with 7 - i; two quad steps finish.
+__device__ __forceinline__ float wave_max_scatter16(const float (&vf)[16], int lane) {
+  uint32_t v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = f_bits(vf[j]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v[j], v[j + 8], false, false);
+    v[j] = max((uint32_t)r[0], (uint32_t)r[1]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v[j], v[j + 4], false, false);
+    v[j] = max((uint32_t)r[0], (uint32_t)r[1]);
+  }
+  const bool b3 = lane & 8;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t send = b3 ? v[j] : v[j + 2], mine = b3 ? v[j + 2] : v[j];
+    v[j] = max(mine, dpp_u32<kDppMirror>(send));
+  }
+  const bool b2 = lane & 4;
+  const uint32_t send = b2 ? v[0] : v[1], mine = b2 ? v[1] : v[0];
+  uint32_t m = max(mine, dpp_u32<kDppHalfMirror>(send));
+  m = max(m, dpp_u32<kDppXor1>(m));
+  return bits_f(max(m, dpp_u32<kDppXor2>(m)));
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t quantize_wave_vector(uint2 raw, float& scale) {
+  float x[D / kWave];
+  unpack_wave_vector<D>(raw, x);
+  return quantize_wave_values<D>(x, scale);
+}
+
+// Rotary position embedding of one wave-held D-vector, rotate-half pairing
+// over the first R dims ([KV] 2.2 names the step; the variant is the usual
+// rotate-half one): for j < R/2, (x_j, x_{j+R/2}) turns by the angle whose
+// cosine and sine are row[j] and row[R/2 + j]:
+//   x_j' = x_j c - x_{j+R/2} s,   x_{j+R/2}' = x_{j+R/2} c + x_j s,
+// each product and the sum / difference rounded to fp32 (no fused
+// multiply-add).  Needs R % (2 D/64) == 0, so that the partner of a lane's
+// element i is element i of the lane R/(2 D/64) further on.  Every lane of
+// the wave must call it (the partner exchange is a wave permute).
+template <int D>
+__device__ __forceinline__ void rope_wave_vector(float (&x)[D / kWave], int lane, const float* row,
+                                                 int R) {
+#pragma clang fp contract(off)
+  constexpr int EPL = D / kWave;
+  const int hl = R / (2 * EPL);  // lanes that hold the first half
+  const bool lower = lane < hl;
+  const bool upper = !lower && lane < 2 * hl;
+  const int partner = lower ? lane + hl : (upper ? lane - hl : lane);
+  float p[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) p[i] = __shfl(x[i], partner, kWave);
+  if (lower || upper) {
+    const int j0 = (lower ? lane : lane - hl) * EPL;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const float c = row[j0 + i], sn = row[R / 2 + j0 + i];
+      const float a = x[i] * c, b = p[i] * sn;
+      x[i] = lower ? a - b : a + b;
+    }
+  }
 }
 
 // The lane's D/64 bf16 elements of a D-vector (see quantize_wave_vector).

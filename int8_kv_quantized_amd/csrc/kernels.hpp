@@ -22,6 +22,10 @@ struct ProducerArgs {
   int8_t* v_cache;
   float* k_scale;
   float* v_scale;
+  // Rotary embedding of Q and K (positions == null: none).
+  const int32_t* positions;  // [T]
+  const float* cos_sin;      // [max_position, rotary_dim]: cos | sin
+  int32_t rotary_dim, max_position;
 };
 
 hipError_t launch_kv_quantize_write(const ProducerArgs& a, hipStream_t stream);

@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_operations():
     names = declared_functions()
-    for op in ("i8kv_kv_quantize_write", "i8kv_paged_decode_int8", "i8kv_prefix_prefill_int8",
-               "i8kv_decode_step_int8"):
+    for op in ("i8kv_kv_quantize_write", "i8kv_kv_quantize_write_rope", "i8kv_paged_decode_int8",
+               "i8kv_prefix_prefill_int8", "i8kv_decode_step_int8"):
         assert op in names
 
 
@@ -95,6 +95,36 @@ def test_descriptor_validation(d, expect):
     assert producer(d) == expect
     assert decode(d) == expect
     assert prefill(d) == expect
+
+
+def producer_rope(d, T=4, pos=FAKE, cs=FAKE, R=64, P_max=4096, **kw):
+    P = lambda x: None if x is None else C.c_void_p(x)
+    a = dict(key=FAKE, value=FAKE, query=None, q8=None, qs=None, slot=FAKE, kc=FAKE, vc=FAKE,
+             ks=FAKE, vs=FAKE)
+    a.update(kw)
+    return _lib().i8kv_kv_quantize_write_rope(
+        None if d is None else C.byref(d), T, P(a["key"]), P(a["value"]), P(a["query"]),
+        P(a["q8"]), P(a["qs"]), P(a["slot"]), P(pos), P(cs), R, P_max, P(a["kc"]), P(a["vc"]),
+        P(a["ks"]), P(a["vs"]), None)
+
+
+@pytest.mark.parametrize("D,kw,expect", [
+    (256, dict(pos=None), NULL), (256, dict(cs=None), NULL), (256, dict(key=None), NULL),
+    (256, dict(query=FAKE, q8=None, qs=FAKE), NULL),
+    (256, dict(P_max=0), INVALID), (256, dict(R=0), INVALID), (256, dict(cs=FAKE + 2), INVALID),
+    (256, dict(T=-1), INVALID),
+    (256, dict(R=260), UNSUPPORTED), (256, dict(R=68), UNSUPPORTED), (256, dict(R=3), UNSUPPORTED),
+    (128, dict(R=66), UNSUPPORTED), (64, dict(R=33), UNSUPPORTED),
+    (256, dict(R=72, T=0), OK), (256, dict(R=256, T=0), OK), (128, dict(R=4, T=0), OK),
+    (64, dict(R=2, T=0), OK), (64, dict(R=64, T=0, cs=FAKE + 4), OK),
+])
+def test_producer_rope_validation(D, kw, expect):
+    assert producer_rope(desc(D=D), **kw) == expect
+
+
+def test_producer_rope_descriptor_checked():
+    assert producer_rope(None) == NULL
+    assert producer_rope(desc(D=100)) == UNSUPPORTED
 
 
 # --- decode -------------------------------------------------------------------

@@ -78,3 +78,46 @@ def test_producer_skips_negative_slots(orc):
     ids=["cfg1", "cfg2_16k", "cfg3_32k", "cfg3_batch16", "cfg4", "cfg5"])
 def test_producer_full_configs(orc, builder):
     _compare(builder(), orc)
+
+
+def _producer_case(orc, T, D, slot_kind, seed, Hq=8, Hkv=2, with_query=True):
+    """Producer over T tokens with a chosen slot pattern, against the oracle."""
+    import int8_kv_quantized_amd as K
+    rng = np.random.default_rng(seed)
+    nb = (T + 15) // 16 + 3
+    key = W.f32_to_bf16_bits(rng.standard_normal((T, Hkv, D), dtype=np.float32))
+    value = W.f32_to_bf16_bits(rng.standard_normal((T, Hkv, D), dtype=np.float32))
+    query = W.f32_to_bf16_bits(rng.standard_normal((T, Hq, D), dtype=np.float32))
+    if slot_kind == "aligned":
+        slots = np.arange(T, dtype=np.int32) + 16
+    elif slot_kind == "offset5":
+        slots = np.arange(T, dtype=np.int32) + 5
+    elif slot_kind == "shuffled":
+        slots = rng.permutation(nb * 16)[:T].astype(np.int32)
+    else:  # aligned with holes: some tokens skip the write
+        slots = np.arange(T, dtype=np.int32)
+        slots[rng.choice(T, max(1, T // 9), replace=False)] = -1
+    say(f"  producer path case T={T} D={D} slots={slot_kind}")
+    d = K.CacheDesc(Hq, Hkv, D, nb)
+    cache = K.PagedCache.allocate(d)
+    q8, qs = K.kv_quantize_write(d, dev(key), dev(value), dev(slots), cache,
+                                 query=dev(query) if with_query else None)
+    ocache = orc.empty_cache(nb, Hkv, D)
+    oq8, oqs = orc.kv_quantize_write(key, value, slots, ocache, num_q_heads=Hq,
+                                     query=query if with_query else None)
+    g = cache_to_np(cache)
+    for k in g:
+        assert_bits_equal(g[k], ocache[k], f"T={T} D={D} {slot_kind} {k}")
+    if with_query:
+        assert_bits_equal(q8.cpu().numpy(), oq8, f"T={T} D={D} {slot_kind} q_int8")
+        assert_bits_equal(qs.cpu().numpy(), oqs, f"T={T} D={D} {slot_kind} q_scale")
+
+
+@pytest.mark.parametrize("T", [1, 15, 63, 64, 65, 200])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("slot_kind", ["aligned", "offset5", "shuffled", "holes"])
+def test_producer_token_counts_and_slot_patterns(orc, T, D, slot_kind):
+    """Both launch shapes (one vector per wave below 64 tokens, 16-token
+    items above) and every store path: whole pages staged through LDS,
+    unaligned or permuted slots token by token, skipped slots, ragged tails."""
+    _producer_case(orc, T, D, slot_kind, seed=T * 7 + D)

@@ -257,6 +257,13 @@ def cfg5_mha_producer_decode(w_group: int = 32, batch: int = 8, new: int = 8,
                          v_laplace=True, w_group=w_group, **MHA)
 
 
+def producer_chunk(tokens: int, w_group: int = 32) -> Workload:
+    """A prefill chunk of `tokens` new tokens of one sequence, every one with
+    its query (the producer's chunk shapes: 2242 and 4096 tokens)."""
+    return make_workload(f"producer_chunk_T{tokens}", seq_lens=[tokens], new_tokens=[tokens],
+                         seed=1100 + tokens % 1000, kind="prefill", w_group=w_group, **GQA)
+
+
 def small_case(name: str = "small", *, seq_lens=(37, 300, 16, 1), new_tokens=None,
                num_q_heads: int = 6, num_kv_heads: int = 2, head_dim: int = 128,
                seed: int = 7, kind: str = "decode", w_group: int = 32,
