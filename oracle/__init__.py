@@ -18,6 +18,7 @@ from . import build as _build
 HERE = Path(__file__).resolve().parent
 ORC_NO_WQUANT = 1
 ORC_EXACT = 2
+ORC_BF16_PV = 4
 
 _P = C.c_void_p
 _I = C.c_int
@@ -60,6 +61,8 @@ class Oracle:
         L.orc_kv_quantize_write.argtypes = [_I] * 6 + [_P] * 10
         L.orc_kv_quantize_write_rope.argtypes = [_I] * 6 + [_P] * 8 + [_I, _I] + [_P] * 4
         L.orc_rope_rotate.argtypes = [_I, _I, _P, _P, _P, _I, _I]
+        L.orc_round_bf16.restype = None
+        L.orc_round_bf16.argtypes = [_P, _I, _P]
         L.orc_paged_decode.argtypes = ([_I] * 6 + [_P] * 7 + [_I, _P, _I, _I, _F, _I, _P])
         L.orc_decode_head.argtypes = ([_I] * 7 + [_P] * 7 + [_I, _P, _I, _I, _F, _I,
                                                               C.POINTER(_DecodeTrace), _P])
@@ -139,6 +142,13 @@ class Oracle:
         if rc:
             raise ValueError(f"orc_kv_quantize_write_rope rejected its arguments ({rc})")
         return q_int8, q_scale
+
+    def round_bf16(self, x):
+        """fp32 -> nearest bf16 (ties to even), as fp32 values."""
+        x = _c(x, np.float32)
+        y = np.empty_like(x)
+        self.lib.orc_round_bf16(_ptr(x), x.size, _ptr(y))
+        return y
 
     def rope_rotate(self, x, positions, cos_sin):
         """The rotation alone: x [n, D] fp32 (a rotated copy is returned)."""

@@ -130,6 +130,18 @@ void add_group_plain(const T* W, int i0, int n, const SeqView& sv, int D,
   }
 }
 
+/* fp32 -> bf16 -> fp32 with round-to-nearest-even on the dropped 16 bits
+ * (finite inputs). */
+float round_to_bf16(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  u &= 0xffff0000u;
+  float r;
+  std::memcpy(&r, &u, 4);
+  return r;
+}
+
 bool geometry_ok(int Hq, int Hkv, int D, int bs, int nb) {
   return Hq > 0 && Hkv > 0 && Hq % Hkv == 0 && D > 0 && D % 16 == 0 && bs > 0 &&
          nb >= 0;
@@ -231,6 +243,11 @@ static int kv_quantize_write_impl(int T, int Hq, int Hkv, int D, int bs, int nb,
   return 0;
 }
 
+/* The bf16 rounding of the BF16-PV ablation, alone (for the pins). */
+void orc_round_bf16(const float* x, int n, float* y) {
+  for (int i = 0; i < n; ++i) y[i] = round_to_bf16(x[i]);
+}
+
 int orc_kv_quantize_write(int T, int Hq, int Hkv, int D, int bs, int nb,
                           const uint16_t* key, const uint16_t* value,
                           const uint16_t* query, int8_t* q_int8, float* q_scale,
@@ -287,7 +304,8 @@ int orc_decode_head(int Hq, int Hkv, int D, int bs, int nb, int seq, int head,
   const int8_t* q = q_int8 + ((size_t)seq * Hq + head) * D;
   const float sq = q_scale[(size_t)seq * Hq + head];
   const bool exact = (flags & ORC_EXACT) != 0;
-  const bool quant_w = (flags & ORC_NO_WQUANT) == 0;
+  const bool bf16_pv = (flags & ORC_BF16_PV) != 0;
+  const bool quant_w = (flags & ORC_NO_WQUANT) == 0 && !bf16_pv;
 
   std::vector<int32_t> acc(L);
   std::vector<float> s(L);
@@ -334,6 +352,8 @@ int orc_decode_head(int Hq, int Hkv, int D, int bs, int nb, int seq, int head,
     for (int i = 0; i < n; ++i) {
       P[i] = e[i] / l;
       W[i] = P[i] * sv.sv(i0 + i);
+      /* BF16-PV ablation: the same W, rounded to bf16, times the int8 V. */
+      if (bf16_pv) W[i] = round_to_bf16(W[i]);
     }
     if (tr && tr->P) std::memcpy(tr->P + i0, P.data(), n * sizeof(float));
     if (tr && tr->W) std::memcpy(tr->W + i0, W.data(), n * sizeof(float));

@@ -39,8 +39,12 @@ extern "C" {
 /* Flags for the attention functions. */
 enum {
   ORC_NO_WQUANT = 1, /* PV uses W itself (no group quantization) */
-  ORC_EXACT = 2      /* scores, exp, P and W in fp64 and W unquantized: exact
+  ORC_EXACT = 2,     /* scores, exp, P and W in fp64 and W unquantized: exact
                         softmax attention over the dequantized int8 cache */
+  ORC_BF16_PV = 4    /* decode only: the BF16-PV ablation -- W = P * sV rounded
+                        to bf16 (nearest, ties to even) instead of group-
+                        quantized to int8, times the int8 V (exact products,
+                        fp64 sum); everything else unchanged */
 };
 
 /* Symmetric int8 quantization of one vector [KV 2.1]:
@@ -50,6 +54,9 @@ void orc_quantize(const float* x, int n, int8_t* q, float* scale);
 
 /* Quantization of one W group [PV 1]: sW = max W / 127, Wq = round(W/sW). */
 void orc_quantize_w(const float* w, int n, int8_t* wq, float* sw);
+
+/* fp32 -> nearest bf16 (ties to even), returned as fp32; finite inputs. */
+void orc_round_bf16(const float* x, int n, float* y);
 
 /* Producer [KV 2.2, 2.3]: quantize K and V per (token, KV head) and write
  * them to the pages at slot_mapping[t] (< 0: skip); quantize Q per

@@ -19,6 +19,8 @@ when the oracle disagrees with what the pages or the mathematics fix:
 * brute force against unquantized fp64 attention within an a-priori bound;
 * special cases with closed-form answers (one token, equal scores, one
   dominant score, empty sequence).
+* the BF16-PV ablation: W rounded to bf16 exactly as torch rounds it, the
+  partition sums recomputed, and the bound against unquantized attention;
 * the rotary embedding against complex multiplication in fp64 (within the
   rounding of two fp32 products and a sum), exact quarter turns and identity
   tables, relative-position invariance of dot products; the producer with
@@ -400,6 +402,73 @@ def pin_decode_bruteforce(orc, G=32, seed=6):
     return worst
 
 
+def pin_bf16_rounding(orc, seed=13):
+    """The oracle's bf16 rounding equals torch's float -> bfloat16 conversion
+    (nearest, ties to even) on random values, exact ties with even and odd
+    kept bits, neighbours of ties, subnormals and large values."""
+    import torch
+    rng = np.random.default_rng(seed)
+    hi = rng.integers(0, 0x7f7f, 4000, dtype=np.uint32) << 16
+    bits = np.concatenate([
+        rng.integers(0, 0x7f7fffff, 4000, dtype=np.uint32),
+        hi | 0x8000, hi | 0x7fff, hi | 0x8001, (hi & 0x00ff0000) | rng.integers(0, 1 << 16, 4000, dtype=np.uint32)])
+    x = bits.view(np.float32)
+    x = np.concatenate([x, -x])
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+    got = orc.round_bf16(x)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), \
+        f"bf16 rounding differs on {int((got != ref).sum())} values"
+
+
+def pin_decode_bf16_pv(orc, seed=12):
+    """The BF16-PV ablation (decode): W = P * sV rounded to bf16 by torch's
+    own conversion (nearest, ties to even) must equal the oracle's W; each
+    partition's o must be sum W * Vq (numpy, fp64); the output stays within
+    the unquantized-fp64 bound with the bf16 rounding term 2^-9 W |Vq| in
+    place of the W-group term; everything before W equals the int8 path."""
+    import torch
+    from oracle import ORC_BF16_PV
+    wl = tiny_decode(seed=seed, seq_lens=(1, 9, 40, 256, 300, 600))
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    ref = decode_reference_fp64(wl)
+    grp = wl.num_q_heads // wl.num_kv_heads
+    for b in range(wl.num_seqs):
+        L = int(wl.seq_lens[b])
+        sl = seq_slots(wl, b)
+        for h in range(wl.num_q_heads):
+            kv = h // grp
+            tr = orc.decode_head(q8, qs, cache, wl.block_tables, wl.seq_lens, b, h,
+                                 flags=ORC_BF16_PV)
+            t8 = orc.decode_head(q8, qs, cache, wl.block_tables, wl.seq_lens, b, h)
+            for k in ("s", "P", "m", "l"):
+                assert np.array_equal(tr[k], t8[k]), f"bf16-PV changed {k} (seq {b} head {h})"
+            w32 = (t8["P"] * sV[sl, kv]).astype(np.float32)
+            wb = torch.from_numpy(w32).to(torch.bfloat16).to(torch.float32).numpy()
+            assert np.array_equal(tr["W"], wb), f"W not bf16-rounded (seq {b} head {h})"
+            vq = V[sl, kv].astype(np.float64)
+            for pp in range(-(-L // 256)):
+                i0, i1 = 256 * pp, min(L, 256 * pp + 256)
+                o = wb[i0:i1].astype(np.float64) @ vq[i0:i1]
+                assert np.allclose(tr["o"][pp], o, rtol=1e-12, atol=1e-12), "o != sum W Vq"
+            # one partition: bound against unquantized fp64 attention
+            big = 256 * -(-L // 256)
+            t1 = orc.decode_head(q8, qs, cache, wl.block_tables, wl.seq_lens, b, h,
+                                 partition=big, flags=ORC_BF16_PV)
+            tok = np.nonzero(wl.token_seq == b)[0]
+            tok = tok[np.argsort(wl.token_pos[tok])]
+            Vorig = W.bf16_bits_to_f32(wl.value[tok, kv]).astype(np.float64)
+            Korig = W.bf16_bits_to_f32(wl.key[tok, kv]).astype(np.float64)
+            qorig = W.bf16_bits_to_f32(wl.query[wl.decode_query_rows()[b], h]).astype(np.float64)
+            Pe = _softmax64(Korig @ qorig / np.sqrt(wl.head_dim))
+            P = t1["P"].astype(np.float64)
+            sVt = sV[sl, kv].astype(np.float64)
+            bound = (np.abs(Pe - P) @ np.abs(Vorig) + (P * sVt / 2).sum()
+                     + (2.0 ** -9 * P * sVt * (1 + 1e-6)) @ np.abs(vq) + 1e-6)
+            err = np.abs(t1["out"] - ref[b, h])
+            assert np.all(err <= bound), f"bf16-PV decode seq {b} head {h}: error above bound"
+
+
 def pin_decode_partition_invariance(orc, G=32, seed=8):
     wl = tiny_decode(seed=seed, seq_lens=(300, 700, 1000, 257, 513))
     cache, q8, qs = orc.fill(wl)
@@ -601,4 +670,5 @@ def pin_prefill_vs_decode(orc, G=32, seed=9):
 ALL_PINS = [pin_quantize_golden, pin_quantize_bruteforce, pin_cache_layout,
             pin_decode_trace, pin_decode_bruteforce, pin_decode_partition_invariance,
             pin_decode_special_cases, pin_prefill_exact, pin_prefill_trace,
-            pin_prefill_vs_decode, pin_rope_rotation, pin_rope_producer]
+            pin_prefill_vs_decode, pin_rope_rotation, pin_rope_producer,
+            pin_bf16_rounding, pin_decode_bf16_pv]

@@ -60,6 +60,11 @@ MUTANTS = {
     "prefill_not_causal": [("const int pos = ctx + (row - query_start_loc[b]);",
                             "const int pos = seq_lens[b] - 1;")],
     "prefill_excludes_self": [("const int nk = pos + 1;", "const int nk = pos > 0 ? pos : 1;")],
+    "bf16_truncates": [("  u += 0x7fffu + ((u >> 16) & 1u);\n", "")],
+    "bf16_ties_up": [("  u += 0x7fffu + ((u >> 16) & 1u);", "  u += 0x8000u;")],
+    "bf16_before_sv": [("      if (bf16_pv) W[i] = round_to_bf16(W[i]);",
+                        "      if (bf16_pv) W[i] = round_to_bf16(P[i]) * sv.sv(i0 + i);")],
+    "bf16_pv_ignored": [("      if (bf16_pv) W[i] = round_to_bf16(W[i]);", "")],
     "rope_inverse_turn": [("    x[j] = a - b;\n    x[j + h] = e + f;",
                            "    x[j] = a + b;\n    x[j + h] = e - f;")],
     "rope_cos_sin_swapped": [("c = cs[j], s = cs[h + j];", "c = cs[h + j], s = cs[j];")],
