@@ -12,7 +12,8 @@ resident in HBM and rotated over enough distinct cache copies (>= 512 MB) to
 defeat the 256 MB last-level cache.  The chunked-prefill path (2048 queries
 over 16384 cached tokens) is timed as well and reported as int8 TOPS, and so
 is the producer alone over 2242- and 4096-token chunks, with and without the
-rotary embedding fused in.
+rotary embedding fused in, and the decode with its int8 PV against a bf16 PV
+(the pages' PV comparison) at 4K, 8K and 16K tokens.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -51,6 +52,8 @@ def parse_args():
     p.add_argument("--min-rotation-mb", type=float, default=512.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-pv-ablation", action="store_true",
+                   help="skip the int8-PV vs bf16-PV decode comparison at 4K/8K/16K")
     p.add_argument("--no-producer-chunks", action="store_true",
                    help="skip the producer-alone timing over 2242- and 4096-token chunks")
     p.add_argument("--prefill-reps", type=int, default=10)
@@ -296,6 +299,67 @@ def time_producer_chunk(tokens, steps=50, min_rotation_mb=512.0):
     return res
 
 
+def time_pv_ablation(L, G=32, steps=50, min_rotation_mb=512.0):
+    """The pages' PV comparison: the same decode call with the int8 PV (W
+    group-quantized, int8 MFMA) and with a bf16 PV (W = P*sV in bf16, int8 V
+    exact in bf16, bf16 MFMA), nothing else changed; a batch-1 decode at
+    L tokens, 24 q / 4 KV heads x 256, 1% of V channels x20.  Returns us per
+    call of each and the speed-up of the int8 PV (bf16 us / int8 us)."""
+    import numpy as np
+    import torch
+
+    import int8_kv_quantized_amd as K
+    import workloads as W
+    wl = W.cfg2_decode(L, G)
+    d = K.CacheDesc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    is_q = np.zeros(wl.num_tokens, bool)
+    is_q[wl.query_token_index] = True
+    hist = np.nonzero(~is_q)[0]
+    qi = wl.query_token_index
+    base = K.PagedCache.allocate(d)
+    K.kv_quantize_write(d, dev(wl.key[hist]), dev(wl.value[hist]), dev(wl.slot_mapping[hist]), base)
+    q8, qs = K.kv_quantize_write(d, dev(wl.key[qi]), dev(wl.value[qi]), dev(wl.slot_mapping[qi]),
+                                 base, query=dev(wl.query))
+    copies = max(1, math.ceil(min_rotation_mb * 1e6 / cache_bytes(d)))
+    caches = [base] + [K.PagedCache(base.k_cache.clone(), base.v_cache.clone(),
+                                    base.k_scale.clone(), base.v_scale.clone())
+                       for _ in range(copies - 1)]
+    bt, sl = dev(wl.block_tables), dev(wl.seq_lens)
+    ws = torch.zeros(K.paged_decode_workspace_bytes(d, wl.num_seqs, wl.max_seq_len),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((wl.num_seqs, d.num_q_heads, d.head_dim), dtype=torch.float32,
+                      device="cuda")
+    calls = {
+        "int8": lambda i: K.paged_decode_int8(d, q8, qs, caches[i % copies], bt, sl,
+                                              wl.max_seq_len, w_group=G, workspace=ws, out=out),
+        "bf16": lambda i: K.paged_decode_bf16pv(d, q8, qs, caches[i % copies], bt, sl,
+                                                wl.max_seq_len, workspace=ws, out=out),
+    }
+    res = {}
+    for name, fn in calls.items():
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        g.replay()
+        runs = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            runs.append(1e3 * e0.elapsed_time(e1) / steps)
+        res[f"{name}_pv_us"] = round(float(np.median(runs)), 3)
+    res["int8_pv_speedup"] = round(res["bf16_pv_us"] / res["int8_pv_us"], 4)
+    return res
+
+
 DECODE_SOURCES = ["int8_kv_quantized_amd/csrc/decode.hip", "int8_kv_quantized_amd/csrc/kernels.hpp",
                   "int8_kv_quantized_amd/csrc/device_common.hpp"]
 
@@ -396,6 +460,12 @@ def main():
             chunks[f"T{T}"] = time_producer_chunk(T)
             log(f"producer chunk T={T}: {chunks[f'T{T}']}")
         extra["producer_chunk"] = chunks
+    if not args.no_pv_ablation:
+        abl = {}
+        for L in (4096, 8192, 16384):
+            abl[f"L{L}"] = time_pv_ablation(L)
+            log(f"PV ablation L={L}: {abl[f'L{L}']}")
+        extra["pv_ablation"] = abl
     if args.sweep:
         sweep = {}
         for name in ["decode_L512", "decode_L4096", "decode_L8192", "decode_L16384",

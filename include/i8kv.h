@@ -1,7 +1,7 @@
 /*
  * i8kv -- paged attention over an INT8 KV cache, native to AMD MI355X (gfx950).
  *
- * C ABI of the library libi8kv.so.  Five calls, on the operations defined on the pages
+ * C ABI of the library libi8kv.so.  Six calls, on the operations defined on the pages
  *   [KV] "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
  *        DCU" (part 1 of the series), and
  *   [PV] "Implementing INT8 PV MMAC on a gfx936 DCU: V-scale fusion,
@@ -16,6 +16,8 @@
  *                              softmax ([KV] 3.2, [PV] 2.1)
  *   i8kv_decode_step_int8   -- the producer of each sequence's newest token
  *                              fused into the decode of that token
+ *   i8kv_paged_decode_bf16pv -- the decode with a bf16 PV product instead of
+ *                              the int8 one (the pages' PV ablation, [PV] 5)
  *
  * Conventions for every call
  *  - Tensor arguments are DEVICE pointers owned by the caller, C-contiguous in
@@ -164,6 +166,25 @@ i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs
                                    float softmax_scale, void* workspace,
                                    size_t workspace_bytes, float* out,
                                    i8kv_stream_t stream);
+
+/*
+ * The BF16-PV ablation of i8kv_paged_decode_int8 ([PV] 5 compares its int8 PV
+ * with a bf16 PV that changes nothing else): the same scores, partitions,
+ * softmax and merge, but each partition's PV is
+ *   o_p[d] = sum_i bf16(W_i) * Vq_i[d],   W_i = P_i * sV_i,
+ * with W rounded to bf16 (nearest, ties to even) instead of group-quantized
+ * to int8, the int8 V taken exactly as bf16, and fp32 accumulation
+ * (v_mfma_f32_16x16x32_bf16).  Arguments, workspace size and errors as
+ * i8kv_paged_decode_int8 without w_group.
+ */
+i8kv_status i8kv_paged_decode_bf16pv(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                     const int8_t* q_int8, const float* q_scale,
+                                     const int8_t* k_cache, const int8_t* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, int32_t max_seq_len,
+                                     int32_t partition_size, float softmax_scale, void* workspace,
+                                     size_t workspace_bytes, float* out, i8kv_stream_t stream);
 
 /*
  * One decode step with the producer fused in: for every sequence s, the

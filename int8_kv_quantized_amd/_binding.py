@@ -74,6 +74,8 @@ def load_library():
     lib.i8kv_paged_decode_int8.restype = C.c_int
     lib.i8kv_paged_decode_int8.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F, P, SZ,
                                                                  P, P])
+    lib.i8kv_paged_decode_bf16pv.restype = C.c_int
+    lib.i8kv_paged_decode_bf16pv.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, F, P, SZ, P, P])
     lib.i8kv_decode_step_int8.restype = C.c_int
     lib.i8kv_decode_step_int8.argtypes = ([D, I32] + [P] * 10 + [I32, P, I32, I32, I32, F, P, SZ,
                                                                   P, P])
@@ -257,17 +259,9 @@ def paged_decode_workspace_bytes(desc: CacheDesc, num_seqs: int, max_seq_len: in
         C.byref(desc), int(num_seqs), int(max_seq_len), int(partition_size)))
 
 
-def paged_decode_int8(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables,
-                      seq_lens, max_seq_len: int, w_group: int = 32,
-                      partition_size: int = 256, softmax_scale: Optional[float] = None,
-                      workspace=None, out=None, stream=None):
-    """Paged decode over the int8 cache; returns ``out`` [S, Hq, D] fp32.
-
-    ``workspace`` must hold paged_decode_workspace_bytes(...) bytes and be
-    256-byte aligned (allocated here if None; contents need no initialization).
-    """
+def _decode_args(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables, seq_lens,
+                 max_seq_len, partition_size, softmax_scale, workspace, out):
     import torch
-    lib = load_library()
     S = int(seq_lens.shape[0]) if _is_tensor(seq_lens) else int(q_int8.shape[0])
     Hq, D = desc.num_q_heads, desc.head_dim
     _check(q_int8, "q_int8", torch.int8, (S, Hq, D))
@@ -288,13 +282,47 @@ def paged_decode_int8(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.float32, device=block_tables.device)
     _check(out, "out", torch.float32, (S, Hq, D))
+    return S, float(softmax_scale), workspace, int(ws_bytes), out
+
+
+def paged_decode_int8(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables,
+                      seq_lens, max_seq_len: int, w_group: int = 32,
+                      partition_size: int = 256, softmax_scale: Optional[float] = None,
+                      workspace=None, out=None, stream=None):
+    """Paged decode over the int8 cache; returns ``out`` [S, Hq, D] fp32.
+
+    ``workspace`` must hold paged_decode_workspace_bytes(...) bytes and be
+    256-byte aligned (allocated here if None; contents need no initialization).
+    """
+    lib = load_library()
+    S, scale, workspace, ws_bytes, out = _decode_args(
+        desc, q_int8, q_scale, cache, block_tables, seq_lens, max_seq_len, partition_size,
+        softmax_scale, workspace, out)
     st = lib.i8kv_paged_decode_int8(
         C.byref(desc), S, _ptr(q_int8), _ptr(q_scale), _ptr(cache.k_cache),
         _ptr(cache.v_cache), _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(partition_size),
-        int(w_group), float(softmax_scale), _ptr(workspace), int(ws_bytes), _ptr(out),
-        _stream(stream))
+        int(w_group), scale, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
     _raise("paged_decode_int8", st)
+    return out
+
+
+def paged_decode_bf16pv(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables,
+                        seq_lens, max_seq_len: int, partition_size: int = 256,
+                        softmax_scale: Optional[float] = None, workspace=None, out=None,
+                        stream=None):
+    """The BF16-PV ablation of paged_decode_int8 (W = P*sV in bf16 times the
+    int8 V, no W groups); same arguments without w_group."""
+    lib = load_library()
+    S, scale, workspace, ws_bytes, out = _decode_args(
+        desc, q_int8, q_scale, cache, block_tables, seq_lens, max_seq_len, partition_size,
+        softmax_scale, workspace, out)
+    st = lib.i8kv_paged_decode_bf16pv(
+        C.byref(desc), S, _ptr(q_int8), _ptr(q_scale), _ptr(cache.k_cache),
+        _ptr(cache.v_cache), _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(partition_size),
+        scale, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
+    _raise("paged_decode_bf16pv", st)
     return out
 
 

@@ -50,6 +50,30 @@ namespace {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 constexpr int kTokStride = kPartition + 4;  // LDS pitch of the score tile (floats)
 constexpr int kWqStride = kPartition + 16;  // LDS pitch of the Wq tile (bytes)
+constexpr int kWbStride = kPartition + 8;   // LDS pitch of the bf16 W tile (elements)
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Eight int8 values (bytes of lo, then hi) as bf16: exact, since |v| <= 128
+// needs at most 8 significant bits; the bf16 bits are the top half of the
+// fp32 value.
+__device__ __forceinline__ v8bf i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  uint32_t f[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    f[k] = __float_as_uint((float)(int8_t)(((k < 4 ? lo : hi) >> (8 * (k & 3))) & 0xffu));
+  v4u w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = (f[2 * k] >> 16) | (f[2 * k + 1] & 0xffff0000u);
+  return __builtin_bit_cast(v8bf, w);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
 }  // namespace
 
 DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t group,
@@ -76,7 +100,7 @@ struct DecodeShape {
   static constexpr int NCW = DW / 16;          // 16-dim PV tiles per wave
 };
 
-template <int D, int G, bool FUSED>
+template <int D, int G, bool FUSED, bool BPV>
 __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_partition_kernel(
     DecodeArgs a) {
   constexpr int NW = DecodeShape<D>::NW;
@@ -95,6 +119,8 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   __shared__ __attribute__((aligned(16))) int8_t s_q[FUSED ? 16 : 1][FUSED ? D : 16];
   __shared__ __attribute__((aligned(16))) int8_t s_nk[FUSED ? D : 16], s_nv[FUSED ? D : 16];
   __shared__ float s_qs[16], s_nsc[2];
+  // BF16-PV ablation: W = P * sV as bf16, [head][token]
+  __shared__ __attribute__((aligned(16))) uint16_t s_wb[BPV ? 16 : 1][BPV ? kWbStride : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -322,6 +348,17 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
       W[i] = P * sv[i];
       am = fmaxf(am, W[i]);
     }
+    if constexpr (BPV) {
+      // the ablation: W itself, rounded to bf16, no group quantization
+      const uint32_t lo = bf16_rne_bits(W[0]) | (bf16_rne_bits(W[1]) << 16);
+      const uint32_t hi = bf16_rne_bits(W[2]) | (bf16_rne_bits(W[3]) << 16);
+      *reinterpret_cast<uint2*>(&s_wb[h][4 * lane]) = make_uint2(lo, hi);
+      if (lane == 0) {
+        s_M[h] = m;
+        s_L[h] = l;
+      }
+      continue;
+    }
     am = group_max<G / 4>(am);  // G consecutive tokens = G/4 consecutive lanes
     const float sw = div_f32_rn(am, 127.0f, 1.0 / 127.0);  // == am / 127 (IEEE)
     uint32_t packed = 0;
@@ -364,8 +401,33 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
 #pragma unroll
     for (int r = 0; r < 4; ++r) o[c][r] = 0.0f;
   const v4i zero = {0, 0, 0, 0};
+  if constexpr (BPV) {
+    // v_mfma_f32_16x16x32_bf16: lane group lg supplies the same 8 tokens to
+    // both operands -- half hf of page 4g + lg -- so each MFMA sums 32 tokens
+    v4f acc[NCW];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+    for (int c = 0; c < NCW; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        v4u wa = v4u{0u, 0u, 0u, 0u};
+        if (lr < grp) wa = *reinterpret_cast<const v4u*>(&s_wb[lr][16 * (4 * g + lg) + 8 * hf]);
+        const v8bf A = __builtin_bit_cast(v8bf, wa);
+#pragma unroll
+        for (int c = 0; c < NCW; ++c) {
+          const v8bf B = i8x8_to_bf16((uint32_t)vb[g][c][2 * hf], (uint32_t)vb[g][c][2 * hf + 1]);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[c], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NCW; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[c][r] = acc[c][r];
+  }
+#pragma unroll
+  for (int g = 0; g < (BPV ? 0 : 4); ++g) {
     const v4i wa = lr < grp ? *reinterpret_cast<const v4i*>(&s_wq[lr * kWqStride + 64 * g + 16 * lg])
                             : zero;
     float s0[4], s1[4];
@@ -495,12 +557,15 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
   dim3 mgrid((unsigned)a.num_q_heads, (unsigned)a.num_seqs, (unsigned)(a.head_dim / 64));
 #define I8KV_DECODE_CASE(DD, GG)                                                             \
-  if (a.head_dim == DD && a.w_group == GG) {                                                 \
-    if (a.new_key)                                                                           \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true>), grid,                \
+  if (a.head_dim == DD && (a.pv_bf16 ? GG == 64 : a.w_group == GG)) {                       \
+    if (a.pv_bf16)                                                                           \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, true>), grid,         \
+                         dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
+    else if (a.new_key)                                                                      \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, false>), grid,         \
                          dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
     else                                                                                     \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false>), grid,               \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, false>), grid,        \
                          dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
     if (a.max_parts > 1)                                                                     \
       hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(kWave), 0, stream, a); \

@@ -44,6 +44,7 @@ DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t grou
 struct DecodeArgs {
   int32_t num_seqs, num_q_heads, num_kv_heads, group, head_dim, num_blocks;
   int32_t max_blocks_per_seq, max_seq_len, w_group;
+  int32_t pv_bf16;  // the BF16-PV ablation (w_group unused)
   float softmax_scale;
   const int8_t* q_int8;
   const float* q_scale;
