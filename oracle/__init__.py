@@ -19,6 +19,7 @@ HERE = Path(__file__).resolve().parent
 ORC_NO_WQUANT = 1
 ORC_EXACT = 2
 ORC_BF16_PV = 4
+ORC_UINT8_W = 8
 
 _P = C.c_void_p
 _I = C.c_int
@@ -58,6 +59,8 @@ class Oracle:
         L.orc_quantize.argtypes = [_P, _I, _P, _P]
         L.orc_quantize_w.restype = None
         L.orc_quantize_w.argtypes = [_P, _I, _P, _P]
+        L.orc_quantize_w_u8.restype = None
+        L.orc_quantize_w_u8.argtypes = [_P, _I, _P, _P]
         L.orc_kv_quantize_write.argtypes = [_I] * 6 + [_P] * 10
         L.orc_kv_quantize_write_rope.argtypes = [_I] * 6 + [_P] * 8 + [_I, _I] + [_P] * 4
         L.orc_rope_rotate.argtypes = [_I, _I, _P, _P, _P, _I, _I]
@@ -87,6 +90,13 @@ class Oracle:
         q = np.zeros(w.shape, np.int8)
         s = np.zeros(1, np.float32)
         self.lib.orc_quantize_w(_ptr(w), w.size, _ptr(q), _ptr(s))
+        return q, np.float32(s[0])
+
+    def quantize_w_u8(self, w: np.ndarray):
+        w = _c(w, np.float32)
+        q = np.zeros(w.shape, np.uint8)
+        s = np.zeros(1, np.float32)
+        self.lib.orc_quantize_w_u8(_ptr(w), w.size, _ptr(q), _ptr(s))
         return q, np.float32(s[0])
 
     # ------------------------------------------------------------------

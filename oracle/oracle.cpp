@@ -119,6 +119,22 @@ void add_group_quantized(const float* W, int i0, int n, const SeqView& sv, int D
   }
 }
 
+/* The UINT8-W variant of one group: sW = max W / 255, Wq = round(W / sW) in
+ * [0, 255], c[d] = sW * sum Wq_i * Vq_i[d] (exact integer inner sum). */
+void add_group_quantized_u8(const float* W, int i0, int n, const SeqView& sv, int D,
+                            double weight, double* o, int8_t* wq_out, float* sw_out) {
+  std::vector<uint8_t> wq(n);
+  float sw = 0.0f;
+  orc_quantize_w_u8(W, n, wq.data(), &sw);
+  if (wq_out) std::memcpy(wq_out, wq.data(), n);
+  if (sw_out) *sw_out = sw;
+  for (int d = 0; d < D; ++d) {
+    int64_t acc = 0;
+    for (int j = 0; j < n; ++j) acc += (int64_t)wq[j] * (int64_t)sv.vq(i0 + j, d);
+    o[d] += weight * (double)sw * (double)acc;
+  }
+}
+
 /* Unquantized W: c[d] = sum_i W_i * Vq_i[d] (used by the invariance pins). */
 template <typename T>
 void add_group_plain(const T* W, int i0, int n, const SeqView& sv, int D,
@@ -169,6 +185,27 @@ void orc_quantize(const float* x, int n, int8_t* q, float* scale) {
     if (r > 127.0f) r = 127.0f;
     if (r < -127.0f) r = -127.0f;
     q[i] = (int8_t)r;
+  }
+}
+
+/* UINT8 W ([PV] 6 names it as the candidate with one more bit, since W >= 0):
+ * sW = max W / 255, Wq = round(W / sW) in [0, 255], ties away from zero;
+ * max W == 0 gives sW = 0 and Wq = 0. */
+void orc_quantize_w_u8(const float* w, int n, uint8_t* wq, float* sw) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) amax = std::max(amax, std::fabs(w[i]));
+  if (amax == 0.0f) {
+    *sw = 0.0f;
+    for (int i = 0; i < n; ++i) wq[i] = 0;
+    return;
+  }
+  const float s = amax / 255.0f;
+  *sw = s;
+  for (int i = 0; i < n; ++i) {
+    float r = std::round(w[i] / s);
+    if (r > 255.0f) r = 255.0f;
+    if (r < 0.0f) r = 0.0f;
+    wq[i] = (uint8_t)r;
   }
 }
 
@@ -305,6 +342,7 @@ int orc_decode_head(int Hq, int Hkv, int D, int bs, int nb, int seq, int head,
   const float sq = q_scale[(size_t)seq * Hq + head];
   const bool exact = (flags & ORC_EXACT) != 0;
   const bool bf16_pv = (flags & ORC_BF16_PV) != 0;
+  const bool u8_w = (flags & ORC_UINT8_W) != 0;
   const bool quant_w = (flags & ORC_NO_WQUANT) == 0 && !bf16_pv;
 
   std::vector<int32_t> acc(L);
@@ -360,7 +398,11 @@ int orc_decode_head(int Hq, int Hkv, int D, int bs, int nb, int seq, int head,
     /* [PV 1, 4] groups of G consecutive tokens, aligned to absolute position. */
     for (int g0 = 0; g0 < n; g0 += w_group) {
       const int gn = std::min(w_group, n - g0);
-      if (quant_w) {
+      if (quant_w && u8_w) {
+        add_group_quantized_u8(&W[g0], i0 + g0, gn, sv, D, 1.0, o,
+                               tr && tr->Wq ? tr->Wq + i0 + g0 : nullptr,
+                               tr && tr->sW ? tr->sW + (i0 + g0) / w_group : nullptr);
+      } else if (quant_w) {
         add_group_quantized(&W[g0], i0 + g0, gn, sv, D, 1.0, o,
                             tr && tr->Wq ? tr->Wq + i0 + g0 : nullptr,
                             tr && tr->sW ? tr->sW + (i0 + g0) / w_group : nullptr);

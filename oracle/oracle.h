@@ -41,10 +41,13 @@ enum {
   ORC_NO_WQUANT = 1, /* PV uses W itself (no group quantization) */
   ORC_EXACT = 2,     /* scores, exp, P and W in fp64 and W unquantized: exact
                         softmax attention over the dequantized int8 cache */
-  ORC_BF16_PV = 4    /* decode only: the BF16-PV ablation -- W = P * sV rounded
+  ORC_BF16_PV = 4,   /* decode only: the BF16-PV ablation -- W = P * sV rounded
                         to bf16 (nearest, ties to even) instead of group-
                         quantized to int8, times the int8 V (exact products,
                         fp64 sum); everything else unchanged */
+  ORC_UINT8_W = 8    /* decode only: W groups quantized to UINT8 (sW = max W /
+                        255, Wq in [0, 255]); the trace's Wq holds the uint8
+                        codes */
 };
 
 /* Symmetric int8 quantization of one vector [KV 2.1]:
@@ -54,6 +57,9 @@ void orc_quantize(const float* x, int n, int8_t* q, float* scale);
 
 /* Quantization of one W group [PV 1]: sW = max W / 127, Wq = round(W/sW). */
 void orc_quantize_w(const float* w, int n, int8_t* wq, float* sw);
+
+/* The UINT8 variant: sW = max W / 255, Wq = round(W/sW) in [0, 255]. */
+void orc_quantize_w_u8(const float* w, int n, uint8_t* wq, float* sw);
 
 /* fp32 -> nearest bf16 (ties to even), returned as fp32; finite inputs. */
 void orc_round_bf16(const float* x, int n, float* y);

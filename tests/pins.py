@@ -19,6 +19,8 @@ when the oracle disagrees with what the pages or the mathematics fix:
 * brute force against unquantized fp64 attention within an a-priori bound;
 * special cases with closed-form answers (one token, equal scores, one
   dominant score, empty sequence).
+* the UINT8-W variant: brute-force nearest codes in [0, 255], group sums
+  recomputed with integers, the bound with sW = max / 255;
 * the BF16-PV ablation: W rounded to bf16 exactly as torch rounds it, the
   partition sums recomputed, and the bound against unquantized attention;
 * the rotary embedding against complex multiplication in fp64 (within the
@@ -402,6 +404,104 @@ def pin_decode_bruteforce(orc, G=32, seed=6):
     return worst
 
 
+def nearest_code_u8(r: np.ndarray) -> np.ndarray:
+    """Brute force: the code in [0, 255] nearest to each r >= 0, ties up."""
+    r = np.asarray(r, np.float64).reshape(-1)
+    codes = np.arange(256, dtype=np.int64)
+    dist = np.abs(r[:, None] - codes[None, :].astype(np.float64))
+    best = dist.min(axis=1, keepdims=True)
+    return np.where(dist == best, codes[None, :], -1).max(axis=1)
+
+
+def pin_quantize_w_u8(orc, seed=14):
+    """UINT8 W groups: sW = max W / 255 in fp32, codes the brute-force nearest
+    of W / sW (fp32) in [0, 255] with ties up, 255 present, zero group -> 0."""
+    rng = np.random.default_rng(seed)
+    for t in range(300):
+        n = int(rng.choice([1, 7, 32, 64]))
+        kind = t % 3
+        if kind == 0:
+            w = rng.random(n).astype(np.float32) * np.float32(10.0 ** rng.uniform(-8, 0))
+        elif kind == 1:  # exact ties: (k + 1/2) * 2^e with a 255 * 2^e maximum
+            e = float(2.0 ** rng.integers(-20, 0))
+            k = rng.integers(0, 255, n).astype(np.float64) + 0.5 * rng.integers(0, 2, n)
+            k[rng.integers(n)] = 255.0
+            w = (k * e).astype(np.float32)
+        else:
+            w = np.zeros(n, np.float32)
+            if n > 1:
+                w[rng.integers(n)] = np.float32(rng.random())
+        q, sw = orc.quantize_w_u8(w)
+        amax = np.float32(w.max())
+        if amax == 0:
+            assert sw == 0 and not q.any(), "zero group must give sW = 0, Wq = 0"
+            continue
+        assert sw.view(np.uint32) == (amax / np.float32(255)).view(np.uint32), "sW != max/255"
+        r = (w / sw).astype(np.float32)
+        assert np.array_equal(q.astype(np.int64), nearest_code_u8(r)), "u8 codes not nearest/ties up"
+        assert q.max() == 255, "non-zero group without a 255 code"
+
+
+def pin_decode_uint8_w(orc, G=32, seed=15):
+    """The UINT8-W decode: everything before W equals the int8 path; Wq are
+    the brute-force nearest codes of W / sW on aligned groups; o is
+    sum_g sW * (Wq . Vq) recomputed with numpy int64; the output stays within
+    the unquantized-attention bound with the sW / 2 term (sW = max / 255),
+    and its error is smaller than the int8 path's on average."""
+    from oracle import ORC_UINT8_W
+    wl = tiny_decode(seed=seed, seq_lens=(1, 17, 64, 256, 300, 700))
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    ref = decode_reference_fp64(wl)
+    grp = wl.num_q_heads // wl.num_kv_heads
+    err8 = err_u = 0.0
+    for b in range(wl.num_seqs):
+        L = int(wl.seq_lens[b])
+        sl = seq_slots(wl, b)
+        for h in range(wl.num_q_heads):
+            kv = h // grp
+            tu = orc.decode_head(q8, qs, cache, wl.block_tables, wl.seq_lens, b, h, w_group=G,
+                                 flags=ORC_UINT8_W)
+            t8 = orc.decode_head(q8, qs, cache, wl.block_tables, wl.seq_lens, b, h, w_group=G)
+            for k in ("s", "P", "W", "m", "l"):
+                assert np.array_equal(tu[k], t8[k]), f"uint8-W changed {k}"
+            wq = tu["Wq"].view(np.uint8).astype(np.int64)
+            vq = V[sl, kv].astype(np.int64)
+            for pp in range(-(-L // 256)):
+                i0, i1 = 256 * pp, min(L, 256 * pp + 256)
+                o = np.zeros(wl.head_dim)
+                for g0 in range(i0, i1, G):
+                    g1 = min(i1, g0 + G)
+                    w = tu["W"][g0:g1]
+                    sw = tu["sW"][g0 // G]
+                    exp_sw = np.float32(w.max()) / np.float32(255) if w.max() > 0 else np.float32(0)
+                    assert sw.view(np.uint32) == np.float32(exp_sw).view(np.uint32), "group sW"
+                    if sw > 0:
+                        r = (w / sw).astype(np.float32)
+                        assert np.array_equal(wq[g0:g1], nearest_code_u8(r)), "group codes"
+                    o += np.float64(sw) * (wq[g0:g1] @ vq[g0:g1]).astype(np.float64)
+                assert np.allclose(tu["o"][pp], o, rtol=1e-12, atol=1e-12), "o != sum sW Wq.Vq"
+            big = 256 * -(-L // 256)
+            t1 = orc.decode_head(q8, qs, cache, wl.block_tables, wl.seq_lens, b, h, w_group=G,
+                                 partition=big, flags=ORC_UINT8_W)
+            tok = np.nonzero(wl.token_seq == b)[0]
+            tok = tok[np.argsort(wl.token_pos[tok])]
+            Vorig = W.bf16_bits_to_f32(wl.value[tok, kv]).astype(np.float64)
+            Korig = W.bf16_bits_to_f32(wl.key[tok, kv]).astype(np.float64)
+            qorig = W.bf16_bits_to_f32(wl.query[wl.decode_query_rows()[b], h]).astype(np.float64)
+            Pe = _softmax64(Korig @ qorig / np.sqrt(wl.head_dim))
+            P = t1["P"].astype(np.float64)
+            sVt = sV[sl, kv].astype(np.float64)
+            sWt = np.repeat(t1["sW"].astype(np.float64), G)[:L]
+            bound = (np.abs(Pe - P) @ np.abs(Vorig) + (P * sVt / 2).sum()
+                     + (sWt / 2 * (1 + 1e-6)) @ np.abs(vq) + 1e-6)
+            err = np.abs(t1["out"] - ref[b, h])
+            assert np.all(err <= bound), f"uint8-W decode seq {b} head {h}: error above bound"
+            err_u += np.abs(tu["out"] - ref[b, h]).mean()
+            err8 += np.abs(t8["out"] - ref[b, h]).mean()
+    assert err_u < err8, f"uint8 W not more accurate on average ({err_u} vs {err8})"
+
+
 def pin_bf16_rounding(orc, seed=13):
     """The oracle's bf16 rounding equals torch's float -> bfloat16 conversion
     (nearest, ties to even) on random values, exact ties with even and odd
@@ -671,4 +771,4 @@ ALL_PINS = [pin_quantize_golden, pin_quantize_bruteforce, pin_cache_layout,
             pin_decode_trace, pin_decode_bruteforce, pin_decode_partition_invariance,
             pin_decode_special_cases, pin_prefill_exact, pin_prefill_trace,
             pin_prefill_vs_decode, pin_rope_rotation, pin_rope_producer,
-            pin_bf16_rounding, pin_decode_bf16_pv]
+            pin_bf16_rounding, pin_decode_bf16_pv, pin_quantize_w_u8, pin_decode_uint8_w]

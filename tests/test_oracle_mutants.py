@@ -60,6 +60,11 @@ MUTANTS = {
     "prefill_not_causal": [("const int pos = ctx + (row - query_start_loc[b]);",
                             "const int pos = seq_lens[b] - 1;")],
     "prefill_excludes_self": [("const int nk = pos + 1;", "const int nk = pos > 0 ? pos : 1;")],
+    "u8_scale_127": [("  const float s = amax / 255.0f;", "  const float s = amax / 127.0f;")],
+    "u8_clamp_127": [("    if (r > 255.0f) r = 255.0f;", "    if (r > 127.0f) r = 127.0f;")],
+    "u8_round_down": [("    float r = std::round(w[i] / s);\n    if (r > 255.0f)",
+                       "    float r = std::floor(w[i] / s);\n    if (r > 255.0f)")],
+    "u8_flag_ignored": [("      if (quant_w && u8_w) {", "      if (false) {")],
     "bf16_truncates": [("  u += 0x7fffu + ((u >> 16) & 1u);\n", "")],
     "bf16_ties_up": [("  u += 0x7fffu + ((u >> 16) & 1u);", "  u += 0x8000u;")],
     "bf16_before_sv": [("      if (bf16_pv) W[i] = round_to_bf16(W[i]);",
