@@ -303,8 +303,9 @@ def time_pv_ablation(L, G=32, steps=50, min_rotation_mb=512.0):
     """The pages' PV comparison: the same decode call with the int8 PV (W
     group-quantized, int8 MFMA) and with a bf16 PV (W = P*sV in bf16, int8 V
     exact in bf16, bf16 MFMA), nothing else changed; a batch-1 decode at
-    L tokens, 24 q / 4 KV heads x 256, 1% of V channels x20.  Returns us per
-    call of each and the speed-up of the int8 PV (bf16 us / int8 us)."""
+    L tokens, 24 q / 4 KV heads x 256, 1% of V channels x20; the UINT8-W
+    variant is timed beside them.  Returns us per call of each and the
+    speed-up of the int8 PV (bf16 us / int8 us)."""
     import numpy as np
     import torch
 
@@ -335,6 +336,9 @@ def time_pv_ablation(L, G=32, steps=50, min_rotation_mb=512.0):
                                               wl.max_seq_len, w_group=G, workspace=ws, out=out),
         "bf16": lambda i: K.paged_decode_bf16pv(d, q8, qs, caches[i % copies], bt, sl,
                                                 wl.max_seq_len, workspace=ws, out=out),
+        "uint8w": lambda i: K.paged_decode_uint8w(d, q8, qs, caches[i % copies], bt, sl,
+                                                  wl.max_seq_len, w_group=G, workspace=ws,
+                                                  out=out),
     }
     res = {}
     for name, fn in calls.items():
@@ -355,7 +359,7 @@ def time_pv_ablation(L, G=32, steps=50, min_rotation_mb=512.0):
             e1.record()
             torch.cuda.synchronize()
             runs.append(1e3 * e0.elapsed_time(e1) / steps)
-        res[f"{name}_pv_us"] = round(float(np.median(runs)), 3)
+        res[f"{name}_us" if name == "uint8w" else f"{name}_pv_us"] = round(float(np.median(runs)), 3)
     res["int8_pv_speedup"] = round(res["bf16_pv_us"] / res["int8_pv_us"], 4)
     return res
 

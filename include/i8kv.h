@@ -1,7 +1,7 @@
 /*
  * i8kv -- paged attention over an INT8 KV cache, native to AMD MI355X (gfx950).
  *
- * C ABI of the library libi8kv.so.  Six calls, on the operations defined on the pages
+ * C ABI of the library libi8kv.so.  Seven calls, on the operations defined on the pages
  *   [KV] "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
  *        DCU" (part 1 of the series), and
  *   [PV] "Implementing INT8 PV MMAC on a gfx936 DCU: V-scale fusion,
@@ -18,6 +18,8 @@
  *                              fused into the decode of that token
  *   i8kv_paged_decode_bf16pv -- the decode with a bf16 PV product instead of
  *                              the int8 one (the pages' PV ablation, [PV] 5)
+ *   i8kv_paged_decode_uint8w -- the decode with UINT8 W groups (the candidate
+ *                              of [PV] 6: W >= 0 gets one more bit)
  *
  * Conventions for every call
  *  - Tensor arguments are DEVICE pointers owned by the caller, C-contiguous in
@@ -184,6 +186,28 @@ i8kv_status i8kv_paged_decode_bf16pv(const i8kv_cache_desc* desc, int32_t num_se
                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                                      const int32_t* seq_lens, int32_t max_seq_len,
                                      int32_t partition_size, float softmax_scale, void* workspace,
+                                     size_t workspace_bytes, float* out, i8kv_stream_t stream);
+
+/*
+ * The decode with UINT8 W groups ([PV] 6 lists UINT8 probabilities as the
+ * candidate with one more bit, since W = P * sV >= 0, but found no correct
+ * and fast UINT8 x INT8 path): as i8kv_paged_decode_int8 except that each
+ * aligned group of w_group tokens uses
+ *   sW = max W / 255,  Wq = round(W / sW) in [0, 255] (ties away from zero),
+ *   o_p += sW * sum_i Wq_i * Vq_i.
+ * gfx950 has only a signed int8 MFMA: the kernel feeds Wq - 128 (an int8)
+ * and adds 128 * sum_i Vq_i back, the column sums coming from the same MFMA
+ * with all-ones rows; the integer result is exact.  Arguments, workspace and
+ * errors as i8kv_paged_decode_int8.
+ */
+i8kv_status i8kv_paged_decode_uint8w(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                     const int8_t* q_int8, const float* q_scale,
+                                     const int8_t* k_cache, const int8_t* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, int32_t max_seq_len,
+                                     int32_t partition_size, int32_t w_group,
+                                     float softmax_scale, void* workspace,
                                      size_t workspace_bytes, float* out, i8kv_stream_t stream);
 
 /*

@@ -12,6 +12,7 @@ fails loudly if the library has not been built -- there is no fallback.
     paged_decode_workspace_bytes(desc, num_seqs, max_seq_len)
     paged_decode_int8(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
     paged_decode_bf16pv(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
+    paged_decode_uint8w(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
     prefix_prefill_int8(desc, q_int8, q_scale, query_start_loc, seq_lens,
                         cache, block_tables, ...)
     decode_step_int8(desc, key, value, query, cache, block_tables, seq_lens, ...)
@@ -28,6 +29,7 @@ from ._binding import (  # noqa: F401
     load_library,
     paged_decode_bf16pv,
     paged_decode_int8,
+    paged_decode_uint8w,
     paged_decode_workspace_bytes,
     prefix_prefill_int8,
     prefix_prefill_workspace_bytes,

@@ -74,6 +74,8 @@ def load_library():
     lib.i8kv_paged_decode_int8.restype = C.c_int
     lib.i8kv_paged_decode_int8.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F, P, SZ,
                                                                  P, P])
+    lib.i8kv_paged_decode_uint8w.restype = C.c_int
+    lib.i8kv_paged_decode_uint8w.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F, P, SZ, P, P])
     lib.i8kv_paged_decode_bf16pv.restype = C.c_int
     lib.i8kv_paged_decode_bf16pv.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, F, P, SZ, P, P])
     lib.i8kv_decode_step_int8.restype = C.c_int
@@ -304,6 +306,25 @@ def paged_decode_int8(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block
         int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(partition_size),
         int(w_group), scale, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
     _raise("paged_decode_int8", st)
+    return out
+
+
+def paged_decode_uint8w(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables,
+                        seq_lens, max_seq_len: int, w_group: int = 32,
+                        partition_size: int = 256, softmax_scale: Optional[float] = None,
+                        workspace=None, out=None, stream=None):
+    """The decode with UINT8 W groups (sW = max W / 255, codes 0..255); same
+    arguments as paged_decode_int8."""
+    lib = load_library()
+    S, scale, workspace, ws_bytes, out = _decode_args(
+        desc, q_int8, q_scale, cache, block_tables, seq_lens, max_seq_len, partition_size,
+        softmax_scale, workspace, out)
+    st = lib.i8kv_paged_decode_uint8w(
+        C.byref(desc), S, _ptr(q_int8), _ptr(q_scale), _ptr(cache.k_cache),
+        _ptr(cache.v_cache), _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(partition_size),
+        int(w_group), scale, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
+    _raise("paged_decode_uint8w", st)
     return out
 
 

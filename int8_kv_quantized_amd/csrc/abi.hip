@@ -146,7 +146,8 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
                        int32_t partition_size, int32_t w_group, float softmax_scale,
                        void* workspace, size_t workspace_bytes, float* out,
-                       const DecodeArgs* fused, i8kv_stream_t stream, bool pv_bf16 = false) {
+                       const DecodeArgs* fused, i8kv_stream_t stream, bool pv_bf16 = false,
+                       bool w_uint8 = false) {
   i8kv_status st = check_desc(desc);
   if (st != I8KV_OK) return st;
   if (!k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !seq_lens || !out)
@@ -186,6 +187,7 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
   a.max_seq_len = max_seq_len;
   a.w_group = w_group;
   a.pv_bf16 = pv_bf16 ? 1 : 0;
+  a.w_uint8 = w_uint8 ? 1 : 0;
   a.softmax_scale = softmax_scale;
   a.q_int8 = fused ? nullptr : q_int8;
   a.q_scale = fused ? nullptr : q_scale;
@@ -233,6 +235,21 @@ i8kv_status i8kv_paged_decode_bf16pv(const i8kv_cache_desc* desc, int32_t num_se
                     block_tables, max_blocks_per_seq, seq_lens, max_seq_len, partition_size,
                     64, softmax_scale, workspace, workspace_bytes, out, nullptr, stream,
                     /*pv_bf16=*/true);
+}
+
+i8kv_status i8kv_paged_decode_uint8w(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                     const int8_t* q_int8, const float* q_scale,
+                                     const int8_t* k_cache, const int8_t* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, int32_t max_seq_len,
+                                     int32_t partition_size, int32_t w_group,
+                                     float softmax_scale, void* workspace,
+                                     size_t workspace_bytes, float* out, i8kv_stream_t stream) {
+  return run_decode(desc, num_seqs, q_int8, q_scale, k_cache, v_cache, k_scale, v_scale,
+                    block_tables, max_blocks_per_seq, seq_lens, max_seq_len, partition_size,
+                    w_group, softmax_scale, workspace, workspace_bytes, out, nullptr, stream,
+                    /*pv_bf16=*/false, /*w_uint8=*/true);
 }
 
 i8kv_status i8kv_decode_step_int8(const i8kv_cache_desc* desc, int32_t num_seqs,

@@ -100,9 +100,15 @@ struct DecodeShape {
   static constexpr int NCW = DW / 16;          // 16-dim PV tiles per wave
 };
 
-template <int D, int G, bool FUSED, bool BPV>
+// PV variants: the method's int8 W groups, the BF16-PV ablation (W = P*sV in
+// bf16), and UINT8 W groups (codes 0..255 against max W / 255).
+enum : int { kPvInt8 = 0, kPvBf16 = 1, kPvUint8 = 2 };
+
+template <int D, int G, bool FUSED, int PVM>
 __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_partition_kernel(
     DecodeArgs a) {
+  constexpr bool BPV = PVM == kPvBf16;
+  constexpr bool U8W = PVM == kPvUint8;
   constexpr int NW = DecodeShape<D>::NW;
   constexpr int NT = NW * kWave;
   constexpr int PPW = DecodeShape<D>::PPW;
@@ -360,13 +366,20 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
       continue;
     }
     am = group_max<G / 4>(am);  // G consecutive tokens = G/4 consecutive lanes
-    const float sw = div_f32_rn(am, 127.0f, 1.0 / 127.0);  // == am / 127 (IEEE)
-    uint32_t packed = 0;
+    // == am / 127 (IEEE), or am / 255 for UINT8 W
+    const float sw = U8W ? div_f32_rn(am, 255.0f, 1.0 / 255.0) : div_f32_rn(am, 127.0f, 1.0 / 127.0);
+    // UINT8 codes c in [0, 255] are stored as c - 128 (int8); the PV adds
+    // 128 * (sum of the group's V) back
+    uint32_t packed = U8W ? 0x80808080u : 0u;
     if (sw > 0.0f) {  // sW = 0 (also when max W / 127 underflows): the group adds 0
       const double rsw = rcp_f64((double)sw);
+      packed = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        packed |= (uint32_t)(round_code(div_f32_rn(W[i], sw, rsw)) & 0xff) << (8 * i);
+      for (int i = 0; i < 4; ++i) {
+        const float q = div_f32_rn(W[i], sw, rsw);
+        const uint32_t c = U8W ? (uint32_t)(fminf(roundf(q), 255.0f)) ^ 0x80u : (uint32_t)round_code(q);
+        packed |= (c & 0xff) << (8 * i);
+      }
     }
     *reinterpret_cast<uint32_t*>(&s_wq[h * kWqStride + 4 * lane]) = packed;
     if (((4 * lane) & (G - 1)) == 0) s_sw[h][(4 * lane) / G] = sw;
@@ -437,17 +450,35 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
       s0[r] = G == 64 ? s_sw[h][g] : s_sw[h][(2 * g) % NGP];
       s1[r] = G == 64 ? 0.0f : s_sw[h][(2 * g + 1) % NGP];
     }
+    // UINT8 W: all-ones A rows give each group's V column sums (masked like W)
+    const v4i ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 #pragma unroll
     for (int c = 0; c < NCW; ++c) {
       if constexpr (G == 64) {
-        const v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa, vb[g][c], zero, 0, 0, 0);
+        v4i acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa, vb[g][c], zero, 0, 0, 0);
+        if constexpr (U8W) {
+          const v4i cs = __builtin_amdgcn_mfma_i32_16x16x64_i8(ones, vb[g][c], zero, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] += cs[r] << 7;
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[c][r] += s0[r] * (float)acc[r];
       } else {
-        const v4i alo = __builtin_amdgcn_mfma_i32_16x16x64_i8(lg < 2 ? wa : zero, vb[g][c], zero,
-                                                              0, 0, 0);
-        const v4i ahi = __builtin_amdgcn_mfma_i32_16x16x64_i8(lg < 2 ? zero : wa, vb[g][c], zero,
-                                                              0, 0, 0);
+        v4i alo = __builtin_amdgcn_mfma_i32_16x16x64_i8(lg < 2 ? wa : zero, vb[g][c], zero,
+                                                        0, 0, 0);
+        v4i ahi = __builtin_amdgcn_mfma_i32_16x16x64_i8(lg < 2 ? zero : wa, vb[g][c], zero,
+                                                        0, 0, 0);
+        if constexpr (U8W) {
+          const v4i clo = __builtin_amdgcn_mfma_i32_16x16x64_i8(lg < 2 ? ones : zero, vb[g][c],
+                                                                zero, 0, 0, 0);
+          const v4i chi = __builtin_amdgcn_mfma_i32_16x16x64_i8(lg < 2 ? zero : ones, vb[g][c],
+                                                                zero, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            alo[r] += clo[r] << 7;
+            ahi[r] += chi[r] << 7;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           o[c][r] += s0[r] * (float)alo[r];
@@ -559,13 +590,16 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
 #define I8KV_DECODE_CASE(DD, GG)                                                             \
   if (a.head_dim == DD && (a.pv_bf16 ? GG == 64 : a.w_group == GG)) {                       \
     if (a.pv_bf16)                                                                           \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, true>), grid,         \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvBf16>), grid,      \
+                         dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
+    else if (a.w_uint8)                                                                      \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvUint8>), grid,     \
                          dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
     else if (a.new_key)                                                                      \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, false>), grid,         \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8>), grid,       \
                          dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
     else                                                                                     \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, false>), grid,        \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8>), grid,      \
                          dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
     if (a.max_parts > 1)                                                                     \
       hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(kWave), 0, stream, a); \
