@@ -13,7 +13,8 @@ defeat the 256 MB last-level cache.  The chunked-prefill path (2048 queries
 over 16384 cached tokens) is timed as well and reported as int8 TOPS, and so
 is the producer alone over 2242- and 4096-token chunks, with and without the
 rotary embedding fused in, and the decode with its int8 PV against a bf16 PV
-(the pages' PV comparison) at 4K, 8K and 16K tokens.
+(the pages' PV comparison) at 4K, 8K and 16K tokens, and 8 causal queries per
+sequence in one decode call on the MHA configuration.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -52,6 +53,8 @@ def parse_args():
     p.add_argument("--min-rotation-mb", type=float, default=512.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-multi-query", action="store_true",
+                   help="skip the 8-queries-per-sequence decode on the MHA configuration")
     p.add_argument("--no-pv-ablation", action="store_true",
                    help="skip the int8-PV vs bf16-PV decode comparison at 4K/8K/16K")
     p.add_argument("--no-producer-chunks", action="store_true",
@@ -364,6 +367,78 @@ def time_pv_ablation(L, G=32, steps=50, min_rotation_mb=512.0):
     return res
 
 
+def time_multi_query(G=32, steps=20, min_rotation_mb=512.0):
+    """The MHA configuration's 8 new tokens per sequence (32 heads x 128, 8
+    sequences, history ~ U{1024..16384}) decoded as 8 causal queries in one
+    paged_decode_ex call (K/V read once), against 8 one-query decode calls
+    over the cut sequences; also the bf16-output variant."""
+    import numpy as np
+    import torch
+
+    import int8_kv_quantized_amd as K
+    import workloads as W
+    wl = W.cfg5_mha_producer_decode(G)
+    nq = 8
+    d = K.CacheDesc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    base = K.PagedCache.allocate(d)
+    K.kv_quantize_write(d, dev(wl.key), dev(wl.value), dev(wl.slot_mapping), base)
+    q8, qs = K.kv_quantize_write(d, dev(wl.key[wl.query_token_index]),
+                                 dev(wl.value[wl.query_token_index]),
+                                 dev(wl.slot_mapping[wl.query_token_index]), base,
+                                 query=dev(wl.query))
+    copies = max(1, math.ceil(min_rotation_mb * 1e6 / cache_bytes(d)))
+    caches = [base] + [K.PagedCache(base.k_cache.clone(), base.v_cache.clone(),
+                                    base.k_scale.clone(), base.v_scale.clone())
+                       for _ in range(copies - 1)]
+    bt, sl = dev(wl.block_tables), dev(wl.seq_lens)
+    cut = [dev(wl.seq_lens - (nq - 1 - j)) for j in range(nq)]
+    q8j = [q8.view(wl.num_seqs, nq, *q8.shape[1:])[:, j].contiguous() for j in range(nq)]
+    qsj = [qs.view(wl.num_seqs, nq, -1)[:, j].contiguous() for j in range(nq)]
+    opts = K.DecodeOpts(256, G, 1.0 / math.sqrt(d.head_dim), 0, nq, 0)
+    ws = torch.zeros(max(K.paged_decode_ex_workspace_bytes(d, opts, wl.num_seqs, wl.max_seq_len),
+                         K.paged_decode_workspace_bytes(d, wl.num_seqs, wl.max_seq_len)),
+                     dtype=torch.uint8, device="cuda")
+    o32 = torch.empty((wl.num_seqs * nq, d.num_q_heads, d.head_dim), dtype=torch.float32,
+                      device="cuda")
+    o16 = torch.empty_like(o32, dtype=torch.bfloat16)
+    oj = torch.empty((wl.num_seqs, d.num_q_heads, d.head_dim), dtype=torch.float32, device="cuda")
+
+    def multi(i, out):
+        K.paged_decode_ex(d, q8, qs, caches[i % copies], bt, sl, wl.max_seq_len,
+                          queries_per_seq=nq, w_group=G, out_bf16=out.dtype == torch.bfloat16,
+                          workspace=ws, out=out)
+
+    def separate(i):
+        for j in range(nq):
+            K.paged_decode_int8(d, q8j[j], qsj[j], caches[i % copies], bt, cut[j],
+                                wl.max_seq_len, w_group=G, workspace=ws, out=oj)
+
+    res = {}
+    for name, fn in (("multi_query_us", lambda i: multi(i, o32)),
+                     ("multi_query_bf16_out_us", lambda i: multi(i, o16)),
+                     ("separate_calls_us", separate)):
+        for i in range(2):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(1e3 * e0.elapsed_time(e1) / steps, 3)
+    eff = wl.effective_kv_bytes()
+    res["multi_query_gbs"] = round(eff / (res["multi_query_us"] * 1e-6) / 1e9, 1)
+    res["speedup_vs_separate"] = round(res["separate_calls_us"] / res["multi_query_us"], 3)
+    return res
+
+
 DECODE_SOURCES = ["int8_kv_quantized_amd/csrc/decode.hip", "int8_kv_quantized_amd/csrc/kernels.hpp",
                   "int8_kv_quantized_amd/csrc/device_common.hpp"]
 
@@ -464,6 +539,10 @@ def main():
             chunks[f"T{T}"] = time_producer_chunk(T)
             log(f"producer chunk T={T}: {chunks[f'T{T}']}")
         extra["producer_chunk"] = chunks
+    if not args.no_multi_query:
+        mq = time_multi_query(args.w_group)
+        log(f"multi-query decode (MHA, 8 seqs x 8 queries): {mq}")
+        extra["multi_query_mha_8x8"] = mq
     if not args.no_pv_ablation:
         abl = {}
         for L in (4096, 8192, 16384):

@@ -1,7 +1,7 @@
 /*
  * i8kv -- paged attention over an INT8 KV cache, native to AMD MI355X (gfx950).
  *
- * C ABI of the library libi8kv.so.  Seven calls, on the operations defined on the pages
+ * C ABI of the library libi8kv.so.  Eight calls, on the operations defined on the pages
  *   [KV] "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
  *        DCU" (part 1 of the series), and
  *   [PV] "Implementing INT8 PV MMAC on a gfx936 DCU: V-scale fusion,
@@ -20,6 +20,8 @@
  *                              the int8 one (the pages' PV ablation, [PV] 5)
  *   i8kv_paged_decode_uint8w -- the decode with UINT8 W groups (the candidate
  *                              of [PV] 6: W >= 0 gets one more bit)
+ *   i8kv_paged_decode_ex    -- the decode with options: PV variant, several
+ *                              causal queries per sequence, bf16 output
  *
  * Conventions for every call
  *  - Tensor arguments are DEVICE pointers owned by the caller, C-contiguous in
@@ -209,6 +211,48 @@ i8kv_status i8kv_paged_decode_uint8w(const i8kv_cache_desc* desc, int32_t num_se
                                      int32_t partition_size, int32_t w_group,
                                      float softmax_scale, void* workspace,
                                      size_t workspace_bytes, float* out, i8kv_stream_t stream);
+
+/* PV variants of i8kv_paged_decode_ex. */
+enum { I8KV_PV_INT8 = 0, I8KV_PV_BF16 = 1, I8KV_PV_UINT8 = 2 };
+
+typedef struct {
+  int32_t partition_size;  /* 256 */
+  int32_t w_group;         /* 32 or 64 (unused by I8KV_PV_BF16) */
+  float softmax_scale;
+  int32_t pv;              /* I8KV_PV_INT8 (the method), _BF16 or _UINT8 (see above) */
+  int32_t queries_per_seq; /* nq >= 1, nq * (Hq / Hkv) <= 16 */
+  int32_t out_bf16;        /* 0: out is fp32; 1: out is bf16 bits (nearest, ties to even) */
+} i8kv_decode_opts;
+
+/* Workspace bytes of i8kv_paged_decode_ex (0 for invalid arguments). */
+size_t i8kv_paged_decode_ex_workspace_bytes(const i8kv_cache_desc* desc,
+                                            const i8kv_decode_opts* opts, int32_t num_seqs,
+                                            int32_t max_seq_len);
+
+/*
+ * The decode with options, in the serving shapes the pages' decode call is
+ * used in ([KV] 3.3 outputs bf16; several new tokens per sequence):
+ *  - nq = queries_per_seq queries per sequence, at positions
+ *    L - nq .. L - 1 (L = seq_lens[s]); query j attends causally to keys
+ *    0 .. L - nq + j, and each is computed exactly as a one-query decode of
+ *    the sequence cut after its own position (256-token partitions of that
+ *    prefix, the same W groups, the same merge); K and V are read once for
+ *    all nq queries.  A query that sees no key (L < nq) outputs zeros.
+ *      q_int8 [S * nq, Hq, D], q_scale [S * nq, Hq]   (row s * nq + j)
+ *      out    [S * nq, Hq, D]
+ *  - pv: the method's int8 W groups, the BF16-PV ablation or UINT8 W.
+ *  - out_bf16: the fp32 result rounded to bf16 (nearest, ties to even).
+ * Workspace: i8kv_paged_decode_ex_workspace_bytes(desc, opts, S, max_seq_len).
+ * Errors: as i8kv_paged_decode_int8; NULL for opts; INVALID_ARG for nq < 1
+ * or out_bf16 not 0/1; UNSUPPORTED for nq * Hq/Hkv > 16 or an unknown pv.
+ */
+i8kv_status i8kv_paged_decode_ex(const i8kv_cache_desc* desc, const i8kv_decode_opts* opts,
+                                 int32_t num_seqs, const int8_t* q_int8, const float* q_scale,
+                                 const int8_t* k_cache, const int8_t* v_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
+                                 size_t workspace_bytes, void* out, i8kv_stream_t stream);
 
 /*
  * One decode step with the producer fused in: for every sequence s, the

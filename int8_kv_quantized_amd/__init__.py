@@ -13,12 +13,15 @@ fails loudly if the library has not been built -- there is no fallback.
     paged_decode_int8(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
     paged_decode_bf16pv(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
     paged_decode_uint8w(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
+    paged_decode_ex(desc, q_int8, q_scale, cache, block_tables, seq_lens, max_seq_len,
+                    queries_per_seq=1, pv="int8", w_group=32, out_bf16=False, ...)
     prefix_prefill_int8(desc, q_int8, q_scale, query_start_loc, seq_lens,
                         cache, block_tables, ...)
     decode_step_int8(desc, key, value, query, cache, block_tables, seq_lens, ...)
 """
 from ._binding import (  # noqa: F401
     CacheDesc,
+    DecodeOpts,
     I8KVError,
     PagedCache,
     abi_version,
@@ -28,6 +31,8 @@ from ._binding import (  # noqa: F401
     lib_path,
     load_library,
     paged_decode_bf16pv,
+    paged_decode_ex,
+    paged_decode_ex_workspace_bytes,
     paged_decode_int8,
     paged_decode_uint8w,
     paged_decode_workspace_bytes,

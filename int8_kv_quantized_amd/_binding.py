@@ -25,6 +25,15 @@ class I8KVError(RuntimeError):
         self.status = status
 
 
+PV_VARIANTS = {"int8": 0, "bf16": 1, "uint8": 2}
+
+
+class DecodeOpts(C.Structure):
+    _fields_ = [("partition_size", C.c_int32), ("w_group", C.c_int32),
+                ("softmax_scale", C.c_float), ("pv", C.c_int32),
+                ("queries_per_seq", C.c_int32), ("out_bf16", C.c_int32)]
+
+
 class CacheDesc(C.Structure):
     _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("block_size", C.c_int32),
@@ -76,6 +85,11 @@ def load_library():
                                                                  P, P])
     lib.i8kv_paged_decode_uint8w.restype = C.c_int
     lib.i8kv_paged_decode_uint8w.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F, P, SZ, P, P])
+    O = C.POINTER(DecodeOpts)
+    lib.i8kv_paged_decode_ex_workspace_bytes.restype = SZ
+    lib.i8kv_paged_decode_ex_workspace_bytes.argtypes = [D, O, I32, I32]
+    lib.i8kv_paged_decode_ex.restype = C.c_int
+    lib.i8kv_paged_decode_ex.argtypes = ([D, O, I32] + [P] * 7 + [I32, P, I32, P, SZ, P, P])
     lib.i8kv_paged_decode_bf16pv.restype = C.c_int
     lib.i8kv_paged_decode_bf16pv.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, F, P, SZ, P, P])
     lib.i8kv_decode_step_int8.restype = C.c_int
@@ -325,6 +339,55 @@ def paged_decode_uint8w(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, blo
         int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(partition_size),
         int(w_group), scale, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
     _raise("paged_decode_uint8w", st)
+    return out
+
+
+def paged_decode_ex_workspace_bytes(desc: CacheDesc, opts: DecodeOpts, num_seqs: int,
+                                    max_seq_len: int) -> int:
+    return int(load_library().i8kv_paged_decode_ex_workspace_bytes(
+        C.byref(desc), C.byref(opts), int(num_seqs), int(max_seq_len)))
+
+
+def paged_decode_ex(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables, seq_lens,
+                    max_seq_len: int, queries_per_seq: int = 1, pv: str = "int8",
+                    w_group: int = 32, out_bf16: bool = False, partition_size: int = 256,
+                    softmax_scale: Optional[float] = None, workspace=None, out=None,
+                    stream=None):
+    """The decode with options: nq causal queries per sequence (rows
+    s * nq + j of q_int8 / q_scale / out), the PV variant ("int8", "bf16",
+    "uint8") and a bf16 output (returned as torch.bfloat16)."""
+    import torch
+    lib = load_library()
+    nq = int(queries_per_seq)
+    S = int(seq_lens.shape[0])
+    Hq, D = desc.num_q_heads, desc.head_dim
+    _check(q_int8, "q_int8", torch.int8, (S * nq, Hq, D))
+    _check(q_scale, "q_scale", torch.float32, (S * nq, Hq))
+    cache.check(desc)
+    _check(block_tables, "block_tables", torch.int32)
+    if not _is_tensor(block_tables) or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError(f"block_tables: expected a ({S}, *) int32 tensor")
+    _check(seq_lens, "seq_lens", torch.int32, (S,))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if pv not in PV_VARIANTS:
+        raise ValueError(f"pv must be one of {sorted(PV_VARIANTS)}")
+    opts = DecodeOpts(int(partition_size), int(w_group), float(softmax_scale), PV_VARIANTS[pv],
+                      nq, 1 if out_bf16 else 0)
+    need = paged_decode_ex_workspace_bytes(desc, opts, S, max_seq_len)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=block_tables.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if _is_tensor(workspace) else need
+    dt = torch.bfloat16 if out_bf16 else torch.float32
+    if out is None:
+        out = torch.empty((S * nq, Hq, D), dtype=dt, device=block_tables.device)
+    _check(out, "out", dt, (S * nq, Hq, D))
+    st = lib.i8kv_paged_decode_ex(
+        C.byref(desc), C.byref(opts), S, _ptr(q_int8), _ptr(q_scale), _ptr(cache.k_cache),
+        _ptr(cache.v_cache), _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), _ptr(workspace),
+        int(ws_bytes), _ptr(out), _stream(stream))
+    _raise("paged_decode_ex", st)
     return out
 
 

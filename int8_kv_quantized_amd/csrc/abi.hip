@@ -147,10 +147,11 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
                        int32_t partition_size, int32_t w_group, float softmax_scale,
                        void* workspace, size_t workspace_bytes, float* out,
                        const DecodeArgs* fused, i8kv_stream_t stream, bool pv_bf16 = false,
-                       bool w_uint8 = false) {
+                       bool w_uint8 = false, int32_t nq = 1, uint16_t* out16 = nullptr) {
   i8kv_status st = check_desc(desc);
   if (st != I8KV_OK) return st;
-  if (!k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !seq_lens || !out)
+  if (!k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !seq_lens ||
+      (!out && !out16))
     return I8KV_ERR_NULL;
   if (!fused && (!q_int8 || !q_scale)) return I8KV_ERR_NULL;
   if (fused && (!fused->new_key || !fused->new_value || !fused->new_query)) return I8KV_ERR_NULL;
@@ -160,9 +161,13 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
   if (!std::isfinite(softmax_scale)) return I8KV_ERR_INVALID_ARG;
   if (partition_size != kPartition || (w_group != 32 && w_group != 64))
     return I8KV_ERR_UNSUPPORTED;
+  if (nq < 1) return I8KV_ERR_INVALID_ARG;
+  if ((int64_t)nq * (desc->num_q_heads / desc->num_kv_heads) > 16 || (fused && nq != 1) ||
+      (int64_t)nq * desc->num_q_heads > 0x7fffffff)
+    return I8KV_ERR_UNSUPPORTED;
   if (max_seq_len > kMaxSeqLen || num_seqs > kMaxGridYZ) return I8KV_ERR_UNSUPPORTED;
   if ((q_int8 && !aligned16(q_int8)) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(out))
+      (out && !aligned16(out)) || (out16 && !aligned16(out16)))
     return I8KV_ERR_INVALID_ARG;
   if (fused && (!aligned16(fused->new_key) || !aligned16(fused->new_value) ||
                 !aligned16(fused->new_query)))
@@ -170,7 +175,7 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
   if (num_seqs == 0) return I8KV_OK;
   const int32_t grp = desc->num_q_heads / desc->num_kv_heads;
   const DecodePlan p =
-      make_decode_plan(num_seqs, desc->num_kv_heads, grp, desc->head_dim, max_seq_len);
+      make_decode_plan(num_seqs, desc->num_kv_heads, grp * nq, desc->head_dim, max_seq_len);
   if (!workspace || workspace_bytes < p.bytes) return I8KV_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8KV_ERR_WORKSPACE;
 
@@ -188,6 +193,7 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
   a.w_group = w_group;
   a.pv_bf16 = pv_bf16 ? 1 : 0;
   a.w_uint8 = w_uint8 ? 1 : 0;
+  a.nq = nq;
   a.softmax_scale = softmax_scale;
   a.q_int8 = fused ? nullptr : q_int8;
   a.q_scale = fused ? nullptr : q_scale;
@@ -197,7 +203,8 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
   a.v_scale = v_scale;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
-  a.out = out;
+  a.out = out16 ? nullptr : out;
+  a.out16 = out16;
   a.part_o = reinterpret_cast<float*>(ws + p.off_part_o);
   a.part_ml = reinterpret_cast<float*>(ws + p.off_part_ml);
   a.max_parts = p.max_parts;
@@ -250,6 +257,39 @@ i8kv_status i8kv_paged_decode_uint8w(const i8kv_cache_desc* desc, int32_t num_se
                     block_tables, max_blocks_per_seq, seq_lens, max_seq_len, partition_size,
                     w_group, softmax_scale, workspace, workspace_bytes, out, nullptr, stream,
                     /*pv_bf16=*/false, /*w_uint8=*/true);
+}
+
+size_t i8kv_paged_decode_ex_workspace_bytes(const i8kv_cache_desc* desc,
+                                            const i8kv_decode_opts* opts, int32_t num_seqs,
+                                            int32_t max_seq_len) {
+  if (!opts || check_desc(desc) != I8KV_OK || num_seqs < 0 || max_seq_len < 0 ||
+      max_seq_len > kMaxSeqLen || opts->partition_size != kPartition ||
+      opts->queries_per_seq < 1 || opts->queries_per_seq > 16)
+    return 0;
+  const DecodePlan p = make_decode_plan(
+      num_seqs, desc->num_kv_heads,
+      desc->num_q_heads / desc->num_kv_heads * opts->queries_per_seq, desc->head_dim, max_seq_len);
+  return p.bytes;
+}
+
+i8kv_status i8kv_paged_decode_ex(const i8kv_cache_desc* desc, const i8kv_decode_opts* opts,
+                                 int32_t num_seqs, const int8_t* q_int8, const float* q_scale,
+                                 const int8_t* k_cache, const int8_t* v_cache,
+                                 const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
+                                 size_t workspace_bytes, void* out, i8kv_stream_t stream) {
+  if (!opts) return I8KV_ERR_NULL;
+  if (opts->pv != I8KV_PV_INT8 && opts->pv != I8KV_PV_BF16 && opts->pv != I8KV_PV_UINT8)
+    return I8KV_ERR_UNSUPPORTED;
+  if (opts->out_bf16 != 0 && opts->out_bf16 != 1) return I8KV_ERR_INVALID_ARG;
+  const bool bf16 = opts->pv == I8KV_PV_BF16;
+  return run_decode(desc, num_seqs, q_int8, q_scale, k_cache, v_cache, k_scale, v_scale,
+                    block_tables, max_blocks_per_seq, seq_lens, max_seq_len,
+                    opts->partition_size, bf16 ? 64 : opts->w_group, opts->softmax_scale,
+                    workspace, workspace_bytes, opts->out_bf16 ? nullptr : static_cast<float*>(out),
+                    nullptr, stream, bf16, opts->pv == I8KV_PV_UINT8, opts->queries_per_seq,
+                    opts->out_bf16 ? static_cast<uint16_t*>(out) : nullptr);
 }
 
 i8kv_status i8kv_decode_step_int8(const i8kv_cache_desc* desc, int32_t num_seqs,

@@ -104,7 +104,7 @@ struct DecodeShape {
 // bf16), and UINT8 W groups (codes 0..255 against max W / 255).
 enum : int { kPvInt8 = 0, kPvBf16 = 1, kPvUint8 = 2 };
 
-template <int D, int G, bool FUSED, int PVM>
+template <int D, int G, bool FUSED, int PVM, bool MQ>
 __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_partition_kernel(
     DecodeArgs a) {
   constexpr bool BPV = PVM == kPvBf16;
@@ -134,6 +134,15 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   const int p = blockIdx.x, kv = blockIdx.y, s = blockIdx.z;
   const int grp = a.group;
   const int Hkv = a.num_kv_heads;
+  // MFMA rows: query qi of the sequence's nq (the newest nq positions), head
+  // hg of the GQA group: row = qi * grp + hg (nq = 1: the group's heads)
+  // (MQ = false: one query per sequence, the rows are the group's heads)
+  const int nq = MQ ? a.nq : 1;
+  const int rows = MQ ? grp * nq : grp;
+  auto qrow = [&](int row) {  // [S * nq, Hq] index of a row's query
+    const int qi = MQ ? row / grp : 0;
+    return ((size_t)s * nq + qi) * a.num_q_heads + (size_t)kv * grp + (row - qi * grp);
+  };
 
   // ---- first round trip: the sequence length, the block-table entries of the
   // pages this thread reads, the queries and their scales.  None of them
@@ -169,9 +178,8 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
             (it == grp ? a.new_key : a.new_value) + ((size_t)s * Hkv + kv) * D, lane);
     }
   } else {
-    const bool vh = lr < grp;
-    const int8_t* qp = a.q_int8 +
-                       ((size_t)s * a.num_q_heads + (size_t)kv * grp + (vh ? lr : 0)) * D + 16 * lg;
+    const bool vh = lr < rows;
+    const int8_t* qp = a.q_int8 + qrow(vh ? lr : 0) * D + 16 * lg;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       qa[c] = *reinterpret_cast<const v4i*>(qp + 64 * c);
@@ -180,8 +188,8 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * lg + r;
-      sq[r] = a.q_scale[(size_t)s * a.num_q_heads + (size_t)kv * grp + min(h, grp - 1)];
-      if (h >= grp) sq[r] = 0.0f;
+      sq[r] = a.q_scale[qrow(min(h, rows - 1))];
+      if (h >= rows) sq[r] = 0.0f;
     }
   }
 
@@ -191,7 +199,12 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
 
   const int L = min(max(L_raw, 0), a.max_seq_len);
   const int P_s = (L + kPartition - 1) / kPartition;
-  float* out_base = a.out + ((size_t)s * a.num_q_heads + (size_t)kv * grp) * D;
+  // a row's output element: fp32, or bf16 (nearest, ties to even)
+  auto put_out = [&](int row, int dim, float v) {
+    const size_t i = qrow(row) * D + dim;
+    if (a.out16) a.out16[i] = (uint16_t)bf16_rne_bits(v);
+    else a.out[i] = v;
+  };
   // the newest token (position L - 1) lives in the sequence's last partition
   const bool newest_here = FUSED && L > 0 && p == P_s - 1;
   if constexpr (FUSED) {
@@ -235,11 +248,21 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   }
   if (L == 0) {
     if (p == 0)
-      for (int i = tid; i < grp * D; i += NT) out_base[i] = 0.0f;
+      for (int i = tid; i < rows * D; i += NT) put_out(i / D, i % D, 0.0f);
     return;
   }
   if (p >= P_s) return;
   const int tok0 = p * kPartition;
+  // per output row r of this lane (rows 4 lg + r): the causal key limit and
+  // the output offset, computed once
+  int vis[4];
+  size_t obase[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = min(4 * lg + r, rows - 1);
+    vis[r] = MQ ? L - nq + h / grp + 1 : L;
+    obase[r] = qrow(h) * D;
+  }
   // Entries past the sequence are clamped to a valid page: what they load is
   // discarded (scores of tokens >= L are -inf and their W and scales are 0).
   auto clamp_page = [&](int pg) { return min(max(pg, 0), a.num_blocks - 1); };
@@ -318,18 +341,19 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * lg + r;
-      if (h < grp) {
+      if (h < rows) {
         float x = (float)qk[j][r] * sq[r];
         x = x * sk[j];
         x = x * a.softmax_scale;
-        s_sc[h * kTokStride + tl] = (tok0 + tl < L) ? x : -INFINITY;
+        // causal: query qi sits at position L - nq + qi and sees keys up to it
+        s_sc[h * kTokStride + tl] = (tok0 + tl < vis[r]) ? x : -INFINITY;
       }
     }
   }
   __syncthreads();
 
   // ---- softmax and W quantization: wave h owns head h, lane l tokens 4l..4l+3
-  for (int h = w; h < grp; h += NW) {
+  for (int h = w; h < rows; h += NW) {
     const float4 x4 = *reinterpret_cast<const float4*>(&s_sc[h * kTokStride + 4 * lane]);
     const float x[4] = {x4.x, x4.y, x4.z, x4.w};
     float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -343,14 +367,16 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
     }
     ls = group_sum<kWave>(ls);
     const float l = (float)ls;
-    const double rl = rcp_f64((double)l);  // l >= 1 (the max term is exp(0) = 1)
+    // l >= 1 (the max term is exp(0) = 1), or 0 for a row that sees no token
+    // of this partition (later queries' keys): then P = W = 0, m = -inf
+    const double rl = l > 0.0f ? rcp_f64((double)l) : 0.0;
     const float4 v4 = *reinterpret_cast<const float4*>(&s_sv[4 * lane]);
     const float sv[4] = {v4.x, v4.y, v4.z, v4.w};
     float W[4];
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float P = div_f32_rn(e[i], l, rl);  // == e / l (IEEE)
+      const float P = l > 0.0f ? div_f32_rn(e[i], l, rl) : 0.0f;  // == e / l (IEEE)
       W[i] = P * sv[i];
       am = fmaxf(am, W[i]);
     }
@@ -425,7 +451,7 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         v4u wa = v4u{0u, 0u, 0u, 0u};
-        if (lr < grp) wa = *reinterpret_cast<const v4u*>(&s_wb[lr][16 * (4 * g + lg) + 8 * hf]);
+        if (lr < rows) wa = *reinterpret_cast<const v4u*>(&s_wb[lr][16 * (4 * g + lg) + 8 * hf]);
         const v8bf A = __builtin_bit_cast(v8bf, wa);
 #pragma unroll
         for (int c = 0; c < NCW; ++c) {
@@ -441,7 +467,7 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   }
 #pragma unroll
   for (int g = 0; g < (BPV ? 0 : 4); ++g) {
-    const v4i wa = lr < grp ? *reinterpret_cast<const v4i*>(&s_wq[lr * kWqStride + 64 * g + 16 * lg])
+    const v4i wa = lr < rows ? *reinterpret_cast<const v4i*>(&s_wq[lr * kWqStride + 64 * g + 16 * lg])
                             : zero;
     float s0[4], s1[4];
 #pragma unroll
@@ -489,20 +515,23 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   }
 
   // ---- output (single partition) or partial --------------------------------------
-  const size_t node = (((size_t)s * Hkv + kv) * a.max_parts + p) * grp;
+  const size_t node = (((size_t)s * Hkv + kv) * a.max_parts + p) * rows;
 #pragma unroll
   for (int c = 0; c < NCW; ++c) {
     const int dim = DecodeShape<D>::DW * w + 16 * c + lr;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * lg + r;
-      if (h < grp) {
-        if (P_s == 1) out_base[(size_t)h * D + dim] = o[c][r];
+      if (h < rows) {
+        if (P_s == 1) {
+          if (a.out16) a.out16[obase[r] + dim] = (uint16_t)bf16_rne_bits(o[c][r]);
+          else a.out[obase[r] + dim] = o[c][r];
+        }
         else a.part_o[(node + h) * D + dim] = o[c][r];
       }
     }
   }
-  if (P_s > 1 && tid < grp) {
+  if (P_s > 1 && tid < rows) {
     a.part_ml[(node + tid) * 2] = s_M[tid];
     a.part_ml[(node + tid) * 2 + 1] = s_L[tid];
   }
@@ -520,14 +549,16 @@ template <int D>
 __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a) {
   constexpr int U = 16;            // partitions per lane per round
   constexpr int RP = 4 * U;        // partitions per round (= 64)
-  const int h = blockIdx.x, s = blockIdx.y, slice = blockIdx.z, lane = threadIdx.x;
-  const int grp = a.group;
-  const int kv = h / grp, hh = h % grp;
+  // blockIdx.x = qi * Hq + h: query qi (of nq) of the sequence, q head h
+  const int qi = blockIdx.x / a.num_q_heads, h = blockIdx.x % a.num_q_heads;
+  const int s = blockIdx.y, slice = blockIdx.z, lane = threadIdx.x;
+  const int grp = a.group, rows = grp * a.nq;
+  const int kv = h / grp, row = qi * grp + h % grp;
   const size_t base = ((size_t)s * a.num_kv_heads + kv) * a.max_parts;
-  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + base * grp + hh;
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + base * rows + row;
   const int col = lane & 15, lg = lane >> 4;
-  const size_t ostride = (size_t)grp * D;
-  const float* po = a.part_o + (base * grp + hh) * D + 64 * slice + 4 * col;
+  const size_t ostride = (size_t)rows * D;
+  const float* po = a.part_o + (base * rows + row) * D + 64 * slice + 4 * col;
   float4 v[U];
   auto issue = [&](int q0) {
 #pragma unroll
@@ -537,14 +568,14 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
     }
   };
   issue(0);
-  const float2 ml0 = ml[(size_t)min(lane, a.max_parts - 1) * grp];
+  const float2 ml0 = ml[(size_t)min(lane, a.max_parts - 1) * rows];
   int L = a.seq_lens[s];
   L = min(max(L, 0), a.max_seq_len);
   const int P_s = (L + kPartition - 1) / kPartition;
   if (P_s <= 1) return;  // written by the partition kernel
 
   float m = lane < P_s ? ml0.x : -INFINITY;
-  for (int q = lane + RP; q < P_s; q += RP) m = fmaxf(m, ml[(size_t)q * grp].x);
+  for (int q = lane + RP; q < P_s; q += RP) m = fmaxf(m, ml[(size_t)q * rows].x);
   const float M = group_max<kWave>(m);
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -552,8 +583,8 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
   for (int q0 = 0; q0 < P_s; q0 += RP) {
     float wl = 0.0f;  // weight of partition q0 + lane
     if (q0 + lane < P_s) {
-      const float2 e = q0 == 0 ? ml0 : ml[(size_t)(q0 + lane) * grp];
-      wl = e.y * expf(e.x - M);
+      const float2 e = q0 == 0 ? ml0 : ml[(size_t)(q0 + lane) * rows];
+      wl = e.y > 0.0f ? e.y * expf(e.x - M) : 0.0f;  // l = 0: a partition this query does not see
     }
     wsum += wl;
     if (q0 > 0) issue(q0);
@@ -577,30 +608,49 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
     r[i] = bits_f(x0) + bits_f(x1);
   }
   if (lane < 16) {
-    const float inv = 1.0f / wsum;
-    reinterpret_cast<float4*>(a.out + ((size_t)s * a.num_q_heads + h) * D + 64 * slice)[lane] =
-        make_float4(r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv);
+    // wsum = 0 only for a query that sees no key at all (seq_len < nq): zeros
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    const size_t o = (((size_t)s * a.nq + qi) * a.num_q_heads + h) * D + 64 * slice;
+    if (a.out16) {
+      reinterpret_cast<uint2*>(a.out16 + o)[lane] =
+          make_uint2(bf16_rne_bits(r[0] * inv) | (bf16_rne_bits(r[1] * inv) << 16),
+                     bf16_rne_bits(r[2] * inv) | (bf16_rne_bits(r[3] * inv) << 16));
+    } else {
+      reinterpret_cast<float4*>(a.out + o)[lane] =
+          make_float4(r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv);
+    }
   }
 }
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
   dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-  dim3 mgrid((unsigned)a.num_q_heads, (unsigned)a.num_seqs, (unsigned)(a.head_dim / 64));
+  dim3 mgrid((unsigned)(a.num_q_heads * a.nq), (unsigned)a.num_seqs, (unsigned)(a.head_dim / 64));
 #define I8KV_DECODE_CASE(DD, GG)                                                             \
   if (a.head_dim == DD && (a.pv_bf16 ? GG == 64 : a.w_group == GG)) {                       \
-    if (a.pv_bf16)                                                                           \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvBf16>), grid,      \
-                         dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
+    const dim3 blk(DecodeShape<DD>::NW * kWave);                                             \
+    const bool mq = a.nq > 1;                                                                \
+    if (a.new_key)                                                                           \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8, false>), grid,\
+                         blk, 0, stream, a);                                                 \
+    else if (a.pv_bf16 && mq)                                                                \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvBf16, true>), grid,\
+                         blk, 0, stream, a);                                                 \
+    else if (a.pv_bf16)                                                                      \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvBf16, false>),     \
+                         grid, blk, 0, stream, a);                                           \
+    else if (a.w_uint8 && mq)                                                                \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvUint8, true>),     \
+                         grid, blk, 0, stream, a);                                           \
     else if (a.w_uint8)                                                                      \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvUint8>), grid,     \
-                         dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
-    else if (a.new_key)                                                                      \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8>), grid,       \
-                         dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvUint8, false>),    \
+                         grid, blk, 0, stream, a);                                           \
+    else if (mq)                                                                             \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, true>), grid,\
+                         blk, 0, stream, a);                                                 \
     else                                                                                     \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8>), grid,      \
-                         dim3(DecodeShape<DD>::NW * kWave), 0, stream, a);                   \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false>),     \
+                         grid, blk, 0, stream, a);                                           \
     if (a.max_parts > 1)                                                                     \
       hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(kWave), 0, stream, a); \
     return hipGetLastError();                                                                \

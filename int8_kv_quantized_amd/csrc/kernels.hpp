@@ -46,6 +46,7 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq, max_seq_len, w_group;
   int32_t pv_bf16;  // the BF16-PV ablation (w_group unused)
   int32_t w_uint8;  // UINT8 W groups (codes 0..255, sW = max W / 255)
+  int32_t nq;       // queries per sequence (the newest nq positions, causal)
   float softmax_scale;
   const int8_t* q_int8;
   const float* q_scale;
@@ -56,6 +57,7 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   float* out;
+  uint16_t* out16;  // bf16 output instead of out (nearest, ties to even)
   // fused step (producer of each sequence's newest token + decode); new_key is
   // null for a plain decode
   const uint16_t* new_key;    // [S, Hkv, D] bf16

@@ -213,6 +213,22 @@ class Oracle:
             raise ValueError(f"orc_paged_decode rejected its arguments ({rc})")
         return out
 
+    def paged_decode_multi(self, q_int8, q_scale, cache, block_tables, seq_lens, *,
+                           num_q_heads, queries_per_seq, w_group=32, partition=256,
+                           softmax_scale=None, flags=0):
+        """Several causal queries per sequence (rows s * nq + j, query j at
+        position L - nq + j): each is the one-query decode of the sequence cut
+        after its own position -- orc_paged_decode over nq "sequences" per
+        sequence, sharing its block table.  No arithmetic of its own."""
+        nq = int(queries_per_seq)
+        sl = _c(seq_lens, np.int32).astype(np.int64)
+        S = sl.shape[0]
+        cut = np.maximum(sl[:, None] - nq + np.arange(nq)[None, :] + 1, 0).reshape(-1)
+        bt = np.repeat(_c(block_tables, np.int32), nq, axis=0)
+        return self.paged_decode(q_int8, q_scale, cache, bt, cut.astype(np.int32),
+                                 num_q_heads=num_q_heads, w_group=w_group, partition=partition,
+                                 softmax_scale=softmax_scale, flags=flags)
+
     def decode_head(self, q_int8, q_scale, cache, block_tables, seq_lens, seq, head, *,
                     w_group=32, partition=256, softmax_scale=None, flags=0):
         """One (seq, q head) with every intermediate; returns a dict."""

@@ -19,6 +19,7 @@ when the oracle disagrees with what the pages or the mathematics fix:
 * brute force against unquantized fp64 attention within an a-priori bound;
 * special cases with closed-form answers (one token, equal scores, one
   dominant score, empty sequence).
+* several causal queries per sequence against numpy fp64 causal attention;
 * the UINT8-W variant: brute-force nearest codes in [0, 255], group sums
   recomputed with integers, the bound with sW = max / 255;
 * the BF16-PV ablation: W rounded to bf16 exactly as torch rounds it, the
@@ -502,6 +503,51 @@ def pin_decode_uint8_w(orc, G=32, seed=15):
     assert err_u < err8, f"uint8 W not more accurate on average ({err_u} vs {err8})"
 
 
+def pin_decode_multi_query(orc, seed=16):
+    """Several causal queries per sequence: with ORC_EXACT each query row must
+    equal exact fp64 softmax attention, computed here with numpy, over the
+    dequantized keys 0 .. its position (L - nq + j); a query past the
+    sequence start (L < nq) gives zeros; nq = 1 is the plain decode."""
+    wl = W.make_workload("multi", seq_lens=[5, 257, 300, 520], new_tokens=[5, 8, 8, 8],
+                         num_q_heads=4, num_kv_heads=2, head_dim=32, seed=seed)
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    nq = 8
+    S = wl.num_seqs
+    # rows s*nq + j: the newest 8 query rows of each sequence (sequence 0 has 5)
+    q8m = np.zeros((S * nq, 4, 32), np.int8)
+    qsm = np.zeros((S * nq, 4), np.float32)
+    for b in range(S):
+        rows = np.arange(wl.query_start_loc[b], wl.query_start_loc[b + 1])
+        q8m[b * nq + nq - len(rows): (b + 1) * nq] = q8[rows]
+        qsm[b * nq + nq - len(rows): (b + 1) * nq] = qs[rows]
+    out = orc.paged_decode_multi(q8m, qsm, cache, wl.block_tables, wl.seq_lens, num_q_heads=4,
+                                 queries_per_seq=nq, flags=ORC_EXACT)
+    scale = wl.softmax_scale
+    for b in range(S):
+        L = int(wl.seq_lens[b])
+        sl = seq_slots(wl, b)
+        for j in range(nq):
+            pos = L - nq + j
+            for h in range(4):
+                kv = h // 2
+                o = out[b * nq + j, h]
+                if pos < 0:
+                    assert not o.any(), "a query before the sequence start must give zeros"
+                    continue
+                k = K[sl[:pos + 1], kv].astype(np.float64) * sK[sl[:pos + 1], kv, None]
+                v = V[sl[:pos + 1], kv].astype(np.float64) * sV[sl[:pos + 1], kv, None]
+                qv = q8m[b * nq + j, h].astype(np.float64) * np.float64(qsm[b * nq + j, h])
+                ref = _softmax64(k @ qv * np.float64(scale)) @ v
+                assert np.abs(o - ref).max() <= 1e-5 * (1 + np.abs(ref).max()), \
+                    f"multi-query row (seq {b}, query {j}, head {h})"
+    one = orc.paged_decode_multi(q8m[nq - 1::nq], qsm[nq - 1::nq], cache, wl.block_tables,
+                                 wl.seq_lens, num_q_heads=4, queries_per_seq=1)
+    ref1 = orc.paged_decode(q8m[nq - 1::nq], qsm[nq - 1::nq], cache, wl.block_tables,
+                            wl.seq_lens, num_q_heads=4)
+    assert np.array_equal(one, ref1), "nq = 1 must be the plain decode"
+
+
 def pin_bf16_rounding(orc, seed=13):
     """The oracle's bf16 rounding equals torch's float -> bfloat16 conversion
     (nearest, ties to even) on random values, exact ties with even and odd
@@ -771,4 +817,5 @@ ALL_PINS = [pin_quantize_golden, pin_quantize_bruteforce, pin_cache_layout,
             pin_decode_trace, pin_decode_bruteforce, pin_decode_partition_invariance,
             pin_decode_special_cases, pin_prefill_exact, pin_prefill_trace,
             pin_prefill_vs_decode, pin_rope_rotation, pin_rope_producer,
-            pin_bf16_rounding, pin_decode_bf16_pv, pin_quantize_w_u8, pin_decode_uint8_w]
+            pin_bf16_rounding, pin_decode_bf16_pv, pin_quantize_w_u8, pin_decode_uint8_w,
+            pin_decode_multi_query]

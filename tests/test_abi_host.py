@@ -26,8 +26,8 @@ def declared_functions():
 def test_header_declares_the_operations():
     names = declared_functions()
     for op in ("i8kv_kv_quantize_write", "i8kv_kv_quantize_write_rope", "i8kv_paged_decode_int8",
-               "i8kv_paged_decode_bf16pv", "i8kv_paged_decode_uint8w", "i8kv_prefix_prefill_int8",
-               "i8kv_decode_step_int8"):
+               "i8kv_paged_decode_bf16pv", "i8kv_paged_decode_uint8w", "i8kv_paged_decode_ex",
+               "i8kv_prefix_prefill_int8", "i8kv_decode_step_int8"):
         assert op in names
 
 
@@ -189,6 +189,44 @@ def decode_uint8w(d, S=1, max_len=512, max_blocks=32, part=256, G=32, ws=FAKE,
 def test_decode_uint8w_validation(kw, expect):
     assert decode_uint8w(desc(), **kw) == expect
     assert decode_uint8w(None) == NULL
+
+
+def decode_ex(d, opts_kw=None, S=1, max_len=512, max_blocks=32, ws=FAKE, ws_bytes=1 << 30,
+              q8=FAKE, out=FAKE, no_opts=False):
+    P = lambda x: None if x is None else C.c_void_p(x)
+    o = dict(partition_size=256, w_group=32, softmax_scale=0.0625, pv=0, queries_per_seq=1,
+             out_bf16=0)
+    o.update(opts_kw or {})
+    opts = K.DecodeOpts(**o)
+    return _lib().i8kv_paged_decode_ex(
+        None if d is None else C.byref(d), None if no_opts else C.byref(opts), S, P(q8), P(FAKE),
+        P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), max_blocks, P(FAKE), max_len, P(ws),
+        ws_bytes, P(out), None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(no_opts=True), NULL), (dict(q8=None), NULL), (dict(out=None), NULL),
+    (dict(opts_kw=dict(pv=3)), UNSUPPORTED), (dict(opts_kw=dict(out_bf16=2)), INVALID),
+    (dict(opts_kw=dict(queries_per_seq=0)), INVALID),
+    (dict(opts_kw=dict(queries_per_seq=3)), UNSUPPORTED),   # 3 * 6 rows > 16
+    (dict(opts_kw=dict(queries_per_seq=2, w_group=48)), UNSUPPORTED),
+    (dict(opts_kw=dict(queries_per_seq=2), ws_bytes=16), WORKSPACE),
+    (dict(S=0, opts_kw=dict(queries_per_seq=2, pv=2, out_bf16=1)), OK),
+    (dict(S=0, opts_kw=dict(pv=1, w_group=7)), OK),          # w_group unused by the bf16 PV
+])
+def test_decode_ex_validation(kw, expect):
+    assert decode_ex(desc(), **kw) == expect
+
+
+def test_decode_ex_workspace_query():
+    o = dict(partition_size=256, w_group=32, softmax_scale=0.0625, pv=0, queries_per_seq=2,
+             out_bf16=0)
+    d = desc()
+    ws = _lib().i8kv_paged_decode_ex_workspace_bytes
+    one = ws(C.byref(d), C.byref(K.DecodeOpts(**dict(o, queries_per_seq=1))), 3, 4096)
+    two = ws(C.byref(d), C.byref(K.DecodeOpts(**o)), 3, 4096)
+    assert one == K.paged_decode_workspace_bytes(d, 3, 4096) and two > one
+    assert _lib().i8kv_paged_decode_ex_workspace_bytes(C.byref(d), None, 3, 4096) == 0
 
 
 def decode_step(d, S=2, key=FAKE, value=FAKE, query=FAKE, q8=None, qs=None, kc=FAKE, vc=FAKE,
