@@ -477,7 +477,8 @@ int orc_prefill_row(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
   const int8_t* q = q_int8 + ((size_t)row * Hq + head) * D;
   const float sq = q_scale[(size_t)row * Hq + head];
   const bool exact = (flags & ORC_EXACT) != 0;
-  const bool quant_w = (flags & ORC_NO_WQUANT) == 0;
+  const bool bf16_pv = (flags & ORC_BF16_PV) != 0;
+  const bool quant_w = (flags & ORC_NO_WQUANT) == 0 && !bf16_pv;
 
   /* [PV 2.1] online softmax over key tiles: state (m, l, o). */
   std::vector<double> o(D, 0.0);
@@ -523,6 +524,8 @@ int orc_prefill_row(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
       psum += (double)pt[j];
       /* [PV 2.1] prefill quantizes the unnormalized W = p~ * sV. */
       W[j] = pt[j] * sv.sv(t0 + j);
+      /* BF16-PV ablation: the same W rounded to bf16, times the int8 V. */
+      if (bf16_pv) W[j] = round_to_bf16(W[j]);
     }
     if (tr && tr->ptil) std::memcpy(tr->ptil + t0, pt.data(), n * sizeof(float));
     /* o = alpha * o + sum p~ sV Vq ; l = alpha * l + sum p~ (unquantized p~). */

@@ -41,10 +41,10 @@ enum {
   ORC_NO_WQUANT = 1, /* PV uses W itself (no group quantization) */
   ORC_EXACT = 2,     /* scores, exp, P and W in fp64 and W unquantized: exact
                         softmax attention over the dequantized int8 cache */
-  ORC_BF16_PV = 4,   /* decode only: the BF16-PV ablation -- W = P * sV rounded
-                        to bf16 (nearest, ties to even) instead of group-
-                        quantized to int8, times the int8 V (exact products,
-                        fp64 sum); everything else unchanged */
+  ORC_BF16_PV = 4,   /* the BF16-PV ablation -- W (decode: P * sV; prefill:
+                        p~ * sV) rounded to bf16 (nearest, ties to even)
+                        instead of group-quantized to int8, times the int8 V
+                        (exact products, fp64 sum); everything else unchanged */
   ORC_UINT8_W = 8    /* decode only: W groups quantized to UINT8 (sW = max W /
                         255, Wq in [0, 255]); the trace's Wq holds the uint8
                         codes */

@@ -22,8 +22,9 @@ when the oracle disagrees with what the pages or the mathematics fix:
 * several causal queries per sequence against numpy fp64 causal attention;
 * the UINT8-W variant: brute-force nearest codes in [0, 255], group sums
   recomputed with integers, the bound with sW = max / 255;
-* the BF16-PV ablation: W rounded to bf16 exactly as torch rounds it, the
-  partition sums recomputed, and the bound against unquantized attention;
+* the BF16-PV ablation (decode and prefill): W rounded to bf16 exactly as
+  torch rounds it, the partition sums / the tile re-assembly recomputed, and
+  the bound against unquantized attention;
 * the rotary embedding against complex multiplication in fp64 (within the
   rounding of two fp32 products and a sum), exact quarter turns and identity
   tables, relative-position invariance of dot products; the producer with
@@ -796,6 +797,52 @@ def pin_prefill_trace(orc, G=32, seed=10, tile=64):
             assert np.all(np.abs(tr["out"] - ref[r, h]) <= bound), "prefill error above bound"
 
 
+def pin_prefill_bf16_pv(orc, seed=17, tile=64):
+    """The prefill BF16-PV ablation: scores, running maxima, p~ and l equal
+    the int8 path's; W = bf16(p~ * sV) as torch rounds it; the output equals
+    the re-assembly sum c_tok W Vq / l and stays within the bound against
+    fp64 causal attention with the bf16 term 2^-9 P sV |Vq|."""
+    import torch
+    from oracle import ORC_BF16_PV
+    wl = tiny_prefill(seed=seed)
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    grp = wl.num_q_heads // wl.num_kv_heads
+    ref = prefill_reference_fp64(wl)
+    args = (q8, qs, wl.query_start_loc, wl.seq_lens, cache, wl.block_tables)
+    for r, b, pos in _prefill_rows(wl)[::4]:
+        for h in range(0, wl.num_q_heads, 3):
+            kv = h // grp
+            tb = orc.prefill_row(*args, r, h, tile=tile, flags=ORC_BF16_PV)
+            t8 = orc.prefill_row(*args, r, h, tile=tile)
+            for k in ("s", "ptil", "m_tile", "l"):
+                assert np.array_equal(tb[k], t8[k]), f"bf16-PV prefill changed {k}"
+            nk = pos + 1
+            sl = seq_slots(wl, b)[:nk]
+            w32 = (tb["ptil"] * sV[sl, kv]).astype(np.float32)
+            wb = torch.from_numpy(w32).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+            m_of = np.zeros(nk)
+            mrun = -np.inf
+            for ti, t0 in enumerate(range(0, nk, tile)):
+                mrun = float(tb["m_tile"][ti])
+                m_of[t0:t0 + tile] = mrun
+            c_tok = np.exp(m_of - m_of[-1])
+            vq = V[sl, kv].astype(np.float64)
+            O = (c_tok * wb) @ vq / tb["l"][0]
+            assert np.all(np.abs(tb["out"] - O) <= 1e-5 * (np.abs(O) + 1e-3)), "o/l re-assembly"
+            tok = np.nonzero(wl.token_seq == b)[0]
+            tok = tok[np.argsort(wl.token_pos[tok])][:nk]
+            Vorig = W.bf16_bits_to_f32(wl.value[tok, kv]).astype(np.float64)
+            Korig = W.bf16_bits_to_f32(wl.key[tok, kv]).astype(np.float64)
+            qorig = W.bf16_bits_to_f32(wl.query[r, h]).astype(np.float64)
+            Pe = _softmax64(Korig @ qorig / np.sqrt(wl.head_dim))
+            P = c_tok * tb["ptil"] / tb["l"][0]
+            sVt = sV[sl, kv].astype(np.float64)
+            bound = (np.abs(Pe - P) @ np.abs(Vorig) + (P * sVt / 2).sum()
+                     + (2.0 ** -9 * P * sVt * (1 + 1e-6)) @ np.abs(vq) + 1e-5)
+            assert np.all(np.abs(tb["out"] - ref[r, h]) <= bound), "bf16-PV prefill above bound"
+
+
 def pin_prefill_vs_decode(orc, G=32, seed=9):
     """A prefill row equals a decode of the same query over its visible keys
     (exactly in real arithmetic; here up to fp32 rounding)."""
@@ -818,4 +865,4 @@ ALL_PINS = [pin_quantize_golden, pin_quantize_bruteforce, pin_cache_layout,
             pin_decode_special_cases, pin_prefill_exact, pin_prefill_trace,
             pin_prefill_vs_decode, pin_rope_rotation, pin_rope_producer,
             pin_bf16_rounding, pin_decode_bf16_pv, pin_quantize_w_u8, pin_decode_uint8_w,
-            pin_decode_multi_query]
+            pin_decode_multi_query, pin_prefill_bf16_pv]

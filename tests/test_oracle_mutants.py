@@ -65,6 +65,9 @@ MUTANTS = {
     "u8_round_down": [("    float r = std::round(w[i] / s);\n    if (r > 255.0f)",
                        "    float r = std::floor(w[i] / s);\n    if (r > 255.0f)")],
     "u8_flag_ignored": [("      if (quant_w && u8_w) {", "      if (false) {")],
+    "prefill_bf16_ignored": [("      if (bf16_pv) W[j] = round_to_bf16(W[j]);", "")],
+    "prefill_bf16_before_sv": [("      if (bf16_pv) W[j] = round_to_bf16(W[j]);",
+                                "      if (bf16_pv) W[j] = round_to_bf16(pt[j]) * sv.sv(t0 + j);")],
     "bf16_truncates": [("  u += 0x7fffu + ((u >> 16) & 1u);\n", "")],
     "bf16_ties_up": [("  u += 0x7fffu + ((u >> 16) & 1u);", "  u += 0x8000u;")],
     "bf16_before_sv": [("      if (bf16_pv) W[i] = round_to_bf16(W[i]);",
