@@ -193,7 +193,7 @@ def time_decode(args, log_prefix=""):
                 decode_us=1e3 * float(np.median(dec_ms)), decode_us_runs=[1e3 * x for x in dec_ms])
 
 
-def time_prefill(reps, G=32, graph=True):
+def time_prefill(reps, G=32, graph=True, bf16pv=False):
     import numpy as np
     import torch
 
@@ -215,7 +215,11 @@ def time_prefill(reps, G=32, graph=True):
     out = torch.empty((q8.shape[0], d.num_q_heads, d.head_dim), dtype=torch.float32,
                       device="cuda")
     chunk = int(qi.shape[0])
-    run = lambda: K.prefix_prefill_int8(d, q8, qs, qsl, sl, cache, bt, chunk, w_group=G, out=out)
+    if bf16pv:  # the BF16-PV ablation of the same call
+        run = lambda: K.prefix_prefill_bf16pv(d, q8, qs, qsl, sl, cache, bt, chunk, out=out)
+    else:
+        run = lambda: K.prefix_prefill_int8(d, q8, qs, qsl, sl, cache, bt, chunk, w_group=G,
+                                            out=out)
     for _ in range(2):
         run()
     torch.cuda.synchronize()
@@ -530,6 +534,10 @@ def main():
         pf = time_prefill(args.prefill_reps, graph=not args.no_graph)
         log(f"prefill {pf['workload']}: {pf['us']:.1f} us, {pf['tops']:.1f} int8 TOPS "
             f"({100 * pf['tops'] / INT8_PEAK_TOPS:.1f}% of peak)")
+        if not args.no_pv_ablation:
+            pb = time_prefill(args.prefill_reps, graph=not args.no_graph, bf16pv=True)
+            log(f"prefill BF16-PV ablation: {pb['us']:.1f} us")
+            extra["prefill_bf16pv_us"] = round(pb["us"], 2)
         extra.update(prefill_us=round(pf["us"], 2), prefill_int8_tops=round(pf["tops"], 2),
                      prefill_frac_of_int8_peak=round(pf["tops"] / INT8_PEAK_TOPS, 4),
                      prefill_ops=pf["ops"])

@@ -1,7 +1,7 @@
 /*
  * i8kv -- paged attention over an INT8 KV cache, native to AMD MI355X (gfx950).
  *
- * C ABI of the library libi8kv.so.  Eight calls, on the operations defined on the pages
+ * C ABI of the library libi8kv.so.  Nine calls, on the operations defined on the pages
  *   [KV] "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
  *        DCU" (part 1 of the series), and
  *   [PV] "Implementing INT8 PV MMAC on a gfx936 DCU: V-scale fusion,
@@ -22,6 +22,7 @@
  *                              of [PV] 6: W >= 0 gets one more bit)
  *   i8kv_paged_decode_ex    -- the decode with options: PV variant, several
  *                              causal queries per sequence, bf16 output
+ *   i8kv_prefix_prefill_bf16pv -- the prefill with a bf16 PV product ([PV] 5)
  *
  * Conventions for every call
  *  - Tensor arguments are DEVICE pointers owned by the caller, C-contiguous in
@@ -315,6 +316,26 @@ i8kv_status i8kv_prefix_prefill_int8(const i8kv_cache_desc* desc, int32_t num_se
                                      float softmax_scale, void* workspace,
                                      size_t workspace_bytes, float* out,
                                      i8kv_stream_t stream);
+
+/*
+ * The BF16-PV ablation of i8kv_prefix_prefill_int8 ([PV] 5): the same scores
+ * and online softmax, but W = p~ * sV is rounded to bf16 (nearest, ties to
+ * even) instead of group-quantized, and o = alpha o + sum_i bf16(W_i) Vq_i
+ * with the int8 V taken exactly as bf16 and fp32 accumulation
+ * (v_mfma_f32_16x16x32_bf16); the output is rescaled whenever the running
+ * maximum grows (64-key tiles).  Arguments and errors as
+ * i8kv_prefix_prefill_int8 without w_group.
+ */
+i8kv_status i8kv_prefix_prefill_bf16pv(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                       int32_t total_q, int32_t max_query_len,
+                                       const int8_t* q_int8, const float* q_scale,
+                                       const int32_t* query_start_loc, const int32_t* seq_lens,
+                                       const int8_t* k_cache, const int8_t* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       float softmax_scale, void* workspace,
+                                       size_t workspace_bytes, float* out,
+                                       i8kv_stream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char* i8kv_status_string(i8kv_status status);

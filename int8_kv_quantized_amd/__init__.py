@@ -17,6 +17,8 @@ fails loudly if the library has not been built -- there is no fallback.
                     queries_per_seq=1, pv="int8", w_group=32, out_bf16=False, ...)
     prefix_prefill_int8(desc, q_int8, q_scale, query_start_loc, seq_lens,
                         cache, block_tables, ...)
+    prefix_prefill_bf16pv(desc, q_int8, q_scale, query_start_loc, seq_lens,
+                          cache, block_tables, ...)
     decode_step_int8(desc, key, value, query, cache, block_tables, seq_lens, ...)
 """
 from ._binding import (  # noqa: F401
@@ -36,6 +38,7 @@ from ._binding import (  # noqa: F401
     paged_decode_int8,
     paged_decode_uint8w,
     paged_decode_workspace_bytes,
+    prefix_prefill_bf16pv,
     prefix_prefill_int8,
     prefix_prefill_workspace_bytes,
     status_string,

@@ -97,6 +97,8 @@ def load_library():
                                                                   P, P])
     lib.i8kv_prefix_prefill_workspace_bytes.restype = SZ
     lib.i8kv_prefix_prefill_workspace_bytes.argtypes = [D, I32, I32]
+    lib.i8kv_prefix_prefill_bf16pv.restype = C.c_int
+    lib.i8kv_prefix_prefill_bf16pv.argtypes = ([D, I32, I32, I32] + [P] * 9 + [I32, F, P, SZ, P, P])
     lib.i8kv_prefix_prefill_int8.restype = C.c_int
     lib.i8kv_prefix_prefill_int8.argtypes = ([D, I32, I32, I32] + [P] * 9 + [I32, I32, F, P, SZ,
                                                                             P, P])
@@ -466,7 +468,7 @@ def prefix_prefill_workspace_bytes(desc: CacheDesc, num_seqs: int, total_q: int)
 def prefix_prefill_int8(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_lens,
                         cache: PagedCache, block_tables, max_query_len: int,
                         w_group: int = 32, softmax_scale: Optional[float] = None,
-                        out=None, workspace=None, stream=None):
+                        out=None, workspace=None, stream=None, _bf16pv=False):
     """Chunked prefill with history; returns ``out`` [total_q, Hq, D] fp32."""
     import torch
     lib = load_library()
@@ -487,11 +489,26 @@ def prefix_prefill_int8(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_l
         out = torch.empty((Tq, Hq, D), dtype=torch.float32, device=q_int8.device)
     _check(out, "out", torch.float32, (Tq, Hq, D))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.i8kv_prefix_prefill_int8(
-        C.byref(desc), S, Tq, int(max_query_len), _ptr(q_int8), _ptr(q_scale),
-        _ptr(query_start_loc), _ptr(seq_lens), _ptr(cache.k_cache), _ptr(cache.v_cache),
-        _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables),
-        int(block_tables.shape[1]), int(w_group), float(softmax_scale), _ptr(workspace),
-        int(ws_bytes), _ptr(out), _stream(stream))
-    _raise("prefix_prefill_int8", st)
+    common = (C.byref(desc), S, Tq, int(max_query_len), _ptr(q_int8), _ptr(q_scale),
+              _ptr(query_start_loc), _ptr(seq_lens), _ptr(cache.k_cache), _ptr(cache.v_cache),
+              _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables),
+              int(block_tables.shape[1]))
+    tail = (float(softmax_scale), _ptr(workspace), int(ws_bytes), _ptr(out), _stream(stream))
+    if _bf16pv:
+        st = lib.i8kv_prefix_prefill_bf16pv(*common, *tail)
+        _raise("prefix_prefill_bf16pv", st)
+    else:
+        st = lib.i8kv_prefix_prefill_int8(*common, int(w_group), *tail)
+        _raise("prefix_prefill_int8", st)
     return out
+
+
+def prefix_prefill_bf16pv(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_lens,
+                          cache: PagedCache, block_tables, max_query_len: int,
+                          softmax_scale: Optional[float] = None, out=None, workspace=None,
+                          stream=None):
+    """The BF16-PV ablation of prefix_prefill_int8 (same arguments without
+    w_group)."""
+    return prefix_prefill_int8(desc, q_int8, q_scale, query_start_loc, seq_lens, cache,
+                               block_tables, max_query_len, softmax_scale=softmax_scale,
+                               out=out, workspace=workspace, stream=stream, _bf16pv=True)

@@ -82,6 +82,62 @@ i8kv_status run_producer(const i8kv_cache_desc* desc, int32_t num_tokens, const 
 
 }  // namespace
 
+namespace {
+
+i8kv_status run_prefill(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                     int32_t total_q, int32_t max_query_len,
+                                     const int8_t* q_int8, const float* q_scale,
+                                     const int32_t* query_start_loc, const int32_t* seq_lens,
+                                     const int8_t* k_cache, const int8_t* v_cache,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     int32_t w_group, float softmax_scale, void* workspace,
+                                     size_t workspace_bytes, float* out,
+                                     i8kv_stream_t stream, bool pv_bf16) {
+  (void)workspace;
+  (void)workspace_bytes;
+  i8kv_status st = check_desc(desc);
+  if (st != I8KV_OK) return st;
+  if (!q_int8 || !q_scale || !query_start_loc || !seq_lens || !k_cache || !v_cache ||
+      !k_scale || !v_scale || !block_tables || !out)
+    return I8KV_ERR_NULL;
+  if (num_seqs < 0 || total_q < 0 || max_query_len < 0 || max_blocks_per_seq <= 0)
+    return I8KV_ERR_INVALID_ARG;
+  if (max_query_len > total_q) return I8KV_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return I8KV_ERR_INVALID_ARG;
+  if (w_group != 32 && w_group != 64) return I8KV_ERR_UNSUPPORTED;
+  if (num_seqs > kMaxGridYZ) return I8KV_ERR_UNSUPPORTED;
+  if (!aligned16(q_int8) || !aligned16(k_cache) || !aligned16(v_cache))
+    return I8KV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q == 0) return I8KV_OK;
+  PrefillArgs a{};
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.max_query_len = max_query_len;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.group = desc->num_q_heads / desc->num_kv_heads;
+  a.head_dim = desc->head_dim;
+  a.num_blocks = desc->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.w_group = w_group;
+  a.pv_bf16 = pv_bf16 ? 1 : 0;
+  a.softmax_scale = softmax_scale;
+  a.q_int8 = q_int8;
+  a.q_scale = q_scale;
+  a.query_start_loc = query_start_loc;
+  a.seq_lens = seq_lens;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.out = out;
+  return from_hip(launch_prefix_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t i8kv_abi_version(void) { return I8KV_ABI_VERSION; }
@@ -334,45 +390,26 @@ i8kv_status i8kv_prefix_prefill_int8(const i8kv_cache_desc* desc, int32_t num_se
                                      int32_t w_group, float softmax_scale, void* workspace,
                                      size_t workspace_bytes, float* out,
                                      i8kv_stream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  i8kv_status st = check_desc(desc);
-  if (st != I8KV_OK) return st;
-  if (!q_int8 || !q_scale || !query_start_loc || !seq_lens || !k_cache || !v_cache ||
-      !k_scale || !v_scale || !block_tables || !out)
-    return I8KV_ERR_NULL;
-  if (num_seqs < 0 || total_q < 0 || max_query_len < 0 || max_blocks_per_seq <= 0)
-    return I8KV_ERR_INVALID_ARG;
-  if (max_query_len > total_q) return I8KV_ERR_INVALID_ARG;
-  if (!std::isfinite(softmax_scale)) return I8KV_ERR_INVALID_ARG;
-  if (w_group != 32 && w_group != 64) return I8KV_ERR_UNSUPPORTED;
-  if (num_seqs > kMaxGridYZ) return I8KV_ERR_UNSUPPORTED;
-  if (!aligned16(q_int8) || !aligned16(k_cache) || !aligned16(v_cache))
-    return I8KV_ERR_INVALID_ARG;
-  if (num_seqs == 0 || total_q == 0) return I8KV_OK;
-  PrefillArgs a{};
-  a.num_seqs = num_seqs;
-  a.total_q = total_q;
-  a.max_query_len = max_query_len;
-  a.num_q_heads = desc->num_q_heads;
-  a.num_kv_heads = desc->num_kv_heads;
-  a.group = desc->num_q_heads / desc->num_kv_heads;
-  a.head_dim = desc->head_dim;
-  a.num_blocks = desc->num_blocks;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.w_group = w_group;
-  a.softmax_scale = softmax_scale;
-  a.q_int8 = q_int8;
-  a.q_scale = q_scale;
-  a.query_start_loc = query_start_loc;
-  a.seq_lens = seq_lens;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  a.block_tables = block_tables;
-  a.out = out;
-  return from_hip(launch_prefix_prefill(a, static_cast<hipStream_t>(stream)));
+  return run_prefill(desc, num_seqs, total_q, max_query_len, q_int8, q_scale, query_start_loc,
+                     seq_lens, k_cache, v_cache, k_scale, v_scale, block_tables,
+                     max_blocks_per_seq, w_group, softmax_scale, workspace, workspace_bytes, out,
+                     stream, false);
+}
+
+i8kv_status i8kv_prefix_prefill_bf16pv(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                       int32_t total_q, int32_t max_query_len,
+                                       const int8_t* q_int8, const float* q_scale,
+                                       const int32_t* query_start_loc, const int32_t* seq_lens,
+                                       const int8_t* k_cache, const int8_t* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       float softmax_scale, void* workspace,
+                                       size_t workspace_bytes, float* out,
+                                       i8kv_stream_t stream) {
+  return run_prefill(desc, num_seqs, total_q, max_query_len, q_int8, q_scale, query_start_loc,
+                     seq_lens, k_cache, v_cache, k_scale, v_scale, block_tables,
+                     max_blocks_per_seq, 64, softmax_scale, workspace, workspace_bytes, out,
+                     stream, true);
 }
 
 }  // extern "C"

@@ -52,28 +52,6 @@ constexpr int kTokStride = kPartition + 4;  // LDS pitch of the score tile (floa
 constexpr int kWqStride = kPartition + 16;  // LDS pitch of the Wq tile (bytes)
 constexpr int kWbStride = kPartition + 8;   // LDS pitch of the bf16 W tile (elements)
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
-// Eight int8 values (bytes of lo, then hi) as bf16: exact, since |v| <= 128
-// needs at most 8 significant bits; the bf16 bits are the top half of the
-// fp32 value.
-__device__ __forceinline__ v8bf i8x8_to_bf16(uint32_t lo, uint32_t hi) {
-  uint32_t f[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    f[k] = __float_as_uint((float)(int8_t)(((k < 4 ? lo : hi) >> (8 * (k & 3))) & 0xffu));
-  v4u w;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = (f[2 * k] >> 16) | (f[2 * k + 1] & 0xffff0000u);
-  return __builtin_bit_cast(v8bf, w);
-}
-
-// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
 }  // namespace
 
 DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t group,

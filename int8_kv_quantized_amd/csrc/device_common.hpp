@@ -27,6 +27,29 @@ __device__ __forceinline__ int quantize_code(float x, float s) {
   return (int)r;
 }
 
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Eight int8 values (bytes of lo, then hi) as bf16: exact, since |v| <= 128
+// needs at most 8 significant bits; the bf16 bits are the top half of the
+// fp32 value.
+__device__ __forceinline__ v8bf i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  uint32_t f[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    f[k] = __float_as_uint((float)(int8_t)(((k < 4 ? lo : hi) >> (8 * (k & 3))) & 0xffu));
+  v4u w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = (f[2 * k] >> 16) | (f[2 * k + 1] & 0xffff0000u);
+  return __builtin_bit_cast(v8bf, w);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 // Code of an already divided value: clamp(round(q), -127, 127).
 __device__ __forceinline__ int round_code(float q) {
   return (int)fminf(fmaxf(roundf(q), -127.0f), 127.0f);

@@ -80,6 +80,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 struct PrefillArgs {
   int32_t num_seqs, total_q, max_query_len, num_q_heads, num_kv_heads, group, head_dim,
       num_blocks, max_blocks_per_seq, w_group;
+  int32_t pv_bf16;  // the BF16-PV ablation (w_group unused)
   float softmax_scale;
   const int8_t* q_int8;
   const float* q_scale;

@@ -94,7 +94,12 @@ struct PrefillTile {
   static constexpr int kPagePieces = D * 16 / 1024;         // pieces per page
 };
 
-template <int D, int G>
+// BPV: the BF16-PV ablation -- W = p~ sV rounded to bf16 (no W groups) times
+// the int8 V taken exactly as bf16, v_mfma_f32_16x16x32_bf16 accumulating
+// straight into O; the output is rescaled at every growth of the running max
+// (as the per-tile reference of the online softmax), since bf16 rounding,
+// unlike the group quantization, depends on the reference.
+template <int D, int G, bool BPV>
 __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs a) {
   constexpr int NC = D / 64;   // 64-dim k-steps of QK
   constexpr int NN = D / 16;   // 16-dim output tiles of PV
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
     }
     // ---- online softmax (base 2, lazy rescale) -------------------------------
     mt = row_max4(mt) * crow;
-    const bool grow = row_ok && mt != -INFINITY && (mt > mref + kLazy || mref == -INFINITY);
+    const bool grow = row_ok && mt != -INFINITY && (mt > mref + (BPV ? 0.0f : kLazy) || mref == -INFINITY);
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float alpha = grow ? (mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mref - mt))
                                : 1.0f;
@@ -292,6 +297,29 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
         mx = fmaxf(mx, Wv[g][j]);
       }
       am[g] = row_max4(mx);
+    }
+    if constexpr (BPV) {
+      // ---- O^T += V^T W^T in bf16 (keys of group g: the lane's 8 W values)
+      const int8_t* vt = s_v[buf];
+      const int voff = 8 * (lg & 1);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        v4u wu;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          wu[k] = bf16_rne_bits(Wv[g][2 * k]) | (bf16_rne_bits(Wv[g][2 * k + 1]) << 16);
+        const v8bf wb = __builtin_bit_cast(v8bf, wu);
+        const int8_t* vp = vt + ((2 * g + (lg >> 1)) * D + lr) * 16 + voff;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) {
+          const uint2 vv = *reinterpret_cast<const uint2*>(vp + 256 * n);
+          v4f c = v4f{O[n][0], O[n][1], O[n][2], O[n][3]};
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16(vv.x, vv.y), wb, c, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[n][i] = c[i];
+        }
+      }
+      return;
     }
     if constexpr (G == 64) am[0] = am[1] = fmaxf(am[0], am[1]);
 #pragma unroll
@@ -372,10 +400,13 @@ hipError_t launch_prefix_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int64_t tiles = (rows + kRows - 1) / kRows;
   dim3 grid((unsigned)tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
   dim3 block(kNW * kWave);
-#define I8KV_PREFILL_CASE(DD, GG)                                                     \
-  if (a.head_dim == DD && a.w_group == GG) {                                          \
-    hipLaunchKernelGGL((prefix_prefill_kernel<DD, GG>), grid, block, 0, stream, a);   \
-    return hipGetLastError();                                                         \
+#define I8KV_PREFILL_CASE(DD, GG)                                                       \
+  if (a.head_dim == DD && (a.pv_bf16 ? GG == 64 : a.w_group == GG)) {                   \
+    if (a.pv_bf16)                                                                      \
+      hipLaunchKernelGGL((prefix_prefill_kernel<DD, GG, true>), grid, block, 0, stream, a); \
+    else                                                                                \
+      hipLaunchKernelGGL((prefix_prefill_kernel<DD, GG, false>), grid, block, 0, stream, a); \
+    return hipGetLastError();                                                           \
   }
   I8KV_PREFILL_CASE(64, 32)
   I8KV_PREFILL_CASE(64, 64)

@@ -27,7 +27,7 @@ def test_header_declares_the_operations():
     names = declared_functions()
     for op in ("i8kv_kv_quantize_write", "i8kv_kv_quantize_write_rope", "i8kv_paged_decode_int8",
                "i8kv_paged_decode_bf16pv", "i8kv_paged_decode_uint8w", "i8kv_paged_decode_ex",
-               "i8kv_prefix_prefill_int8", "i8kv_decode_step_int8"):
+               "i8kv_prefix_prefill_int8", "i8kv_prefix_prefill_bf16pv", "i8kv_decode_step_int8"):
         assert op in names
 
 
