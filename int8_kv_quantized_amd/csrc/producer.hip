@@ -79,12 +79,13 @@ struct ProducerStage {
 template <int D, int TPW, bool ROPE>
 __device__ __forceinline__ void producer_load(const ProducerArgs& a, const ProducerItem& it,
                                               int lane, ProducerStage<TPW>& st) {
-#pragma unroll
-  for (int i = 0; i < TPW; ++i)
-    st.raw[i] = load_wave_vector<D>(it.src + min(i, it.nt - 1) * it.stride, lane);
+  // slot and position first: waiting for them then leaves the bulk in flight
   const int64_t tl = it.t0 + min(lane, it.nt - 1);
   st.slot = a.slot_mapping[tl];
   if constexpr (ROPE) st.pos = a.positions[tl];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+    st.raw[i] = load_wave_vector<D>(it.src + min(i, it.nt - 1) * it.stride, lane);
 }
 
 // Lane i's cache slot for token i, or -1 for no write: lanes past the item,
