@@ -28,7 +28,7 @@ namespace i8kv {
 
 constexpr int kProducerWaves = 4;      // waves per workgroup
 constexpr int kChunkTokens = 16;       // TPW of the chunk kernel
-constexpr int kChunkMinTokens = 64;    // fewer tokens: one vector per wave
+constexpr int kChunkMinTokens = 128;   // fewer tokens: one vector per wave (lower latency)
 
 // One work item: vector kind `kind` (0 K, 1 V, 2 Q) of head h for the tokens
 // t0 .. t0 + nt - 1; src points at token t0's vector, stride is the distance
