@@ -73,6 +73,10 @@ class Oracle:
                                                                 _P, _I, _P])
         L.orc_prefill_row.argtypes = ([_I] * 9 + [_P] * 9 + [_I, _I, _I, _F, _I,
                                                              C.POINTER(_PrefillTrace), _P])
+        L.orc_paged_decode_bf16qk.argtypes = ([_I] * 6 + [_P] * 6 + [_I, _P, _I, _I, _F, _I,
+                                                                     _P])
+        L.orc_prefix_prefill_bf16qk.argtypes = ([_I] * 7 + [_P] * 8 + [_I, _I, _I, _F, _I,
+                                                                       _P, _I, _P])
 
     # ------------------------------------------------------------------
     def expf(self, x: float) -> float:
@@ -213,6 +217,26 @@ class Oracle:
             raise ValueError(f"orc_paged_decode rejected its arguments ({rc})")
         return out
 
+    def paged_decode_bf16qk(self, q_bf16, cache, block_tables, seq_lens, *, w_group=32,
+                            partition=256, softmax_scale=None, flags=0):
+        """BF16-QK ablation: the bf16 query (uint16 bits [S, Hq, D], not
+        quantized) against the int8 K codes; the rest as paged_decode."""
+        q = _c(q_bf16, np.uint16)
+        bt = _c(block_tables, np.int32)
+        sl = _c(seq_lens, np.int32)
+        nb, Hkv, _, bs, _ = cache["k_cache"].shape
+        S, Hq, D = q.shape
+        if softmax_scale is None:
+            softmax_scale = float(np.float32(1.0 / np.sqrt(D)))
+        out = np.zeros((S, Hq, D), np.float32)
+        rc = self.lib.orc_paged_decode_bf16qk(
+            Hq, Hkv, D, bs, nb, S, _ptr(q), _ptr(cache["k_cache"]), _ptr(cache["v_cache"]),
+            _ptr(cache["k_scale"]), _ptr(cache["v_scale"]), _ptr(bt), bt.shape[1], _ptr(sl),
+            partition, w_group, softmax_scale, flags, _ptr(out))
+        if rc:
+            raise ValueError(f"orc_paged_decode_bf16qk rejected its arguments ({rc})")
+        return out
+
     def paged_decode_multi(self, q_int8, q_scale, cache, block_tables, seq_lens, *,
                            num_q_heads, queries_per_seq, w_group=32, partition=256,
                            softmax_scale=None, flags=0):
@@ -283,6 +307,30 @@ class Oracle:
             flags, _ptr(r), 0 if r is None else r.shape[0], _ptr(out))
         if rc:
             raise ValueError(f"orc_prefix_prefill rejected its arguments ({rc})")
+        return out
+
+    def prefix_prefill_bf16qk(self, q_bf16, query_start_loc, seq_lens, cache, block_tables,
+                              *, w_group=32, tile=256, softmax_scale=None, flags=0, rows=None,
+                              out=None):
+        """BF16-QK ablation of prefix_prefill: q_bf16 uint16 bits [Tq, Hq, D]."""
+        q = _c(q_bf16, np.uint16)
+        qsl = _c(query_start_loc, np.int32)
+        sl = _c(seq_lens, np.int32)
+        bt = _c(block_tables, np.int32)
+        nb, Hkv, _, bs, _ = cache["k_cache"].shape
+        Tq, Hq, D = q.shape
+        if softmax_scale is None:
+            softmax_scale = float(np.float32(1.0 / np.sqrt(D)))
+        if out is None:
+            out = np.zeros((Tq, Hq, D), np.float32)
+        r = None if rows is None else _c(rows, np.int32)
+        rc = self.lib.orc_prefix_prefill_bf16qk(
+            Hq, Hkv, D, bs, nb, sl.shape[0], Tq, _ptr(q), _ptr(qsl), _ptr(sl),
+            _ptr(cache["k_cache"]), _ptr(cache["v_cache"]), _ptr(cache["k_scale"]),
+            _ptr(cache["v_scale"]), _ptr(bt), bt.shape[1], tile, w_group, softmax_scale, flags,
+            _ptr(r), 0 if r is None else r.shape[0], _ptr(out))
+        if rc:
+            raise ValueError(f"orc_prefix_prefill_bf16qk rejected its arguments ({rc})")
         return out
 
     def prefill_row(self, q_int8, q_scale, query_start_loc, seq_lens, cache,

@@ -103,6 +103,47 @@ double score_f64(int32_t acc, float sq, float sk, float softmax_scale) {
   return (double)acc * (double)sq * (double)sk * (double)softmax_scale;
 }
 
+/* BF16-QK ablation (the QK half of the comparison at the matrix-block
+ * boundary [KV 4]; [PV 5] switches the PV half): the query is not quantized
+ * and its bf16 values meet the int8 K codes exactly.  Each product has at
+ * most 16 significant bits, the sum over d is taken in fp64 and rounded once
+ * to fp32, and the score is (dot * sK) * softmax_scale in fp32, the int8
+ * path's formula with acc * sQ replaced by the dot product. */
+double qk_dot_bf16(const uint16_t* q, const SeqView& sv, int i, int D) {
+  double acc = 0.0;
+  for (int d = 0; d < D; ++d) acc += (double)bf16_to_float(q[d]) * (double)sv.kq(i, d);
+  return acc;
+}
+
+float score_bf16qk_f32(double dot, float sk, float softmax_scale) {
+  float s = (float)dot;
+  s = s * sk;
+  s = s * softmax_scale;
+  return s;
+}
+
+/* The query of one (row, q head): int8 codes and their scale, or (BF16-QK)
+ * the bf16 values. */
+struct Query {
+  const int8_t* q8;
+  float sq;
+  const uint16_t* q16;
+
+  void score(const SeqView& sv, int i, int D, float softmax_scale, float* s, double* s64,
+             int32_t* acc) const {
+    if (q16) {
+      const double dot = qk_dot_bf16(q16, sv, i, D);
+      *s = score_bf16qk_f32(dot, sv.sk(i), softmax_scale);
+      *s64 = dot * (double)sv.sk(i) * (double)softmax_scale;
+      *acc = 0;
+      return;
+    }
+    *acc = qk_acc(q8, sv, i, D);
+    *s = score_f32(*acc, sq, sv.sk(i), softmax_scale);
+    *s64 = score_f64(*acc, sq, sv.sk(i), softmax_scale);
+  }
+};
+
 /* Contribution of one W group to the output [PV 1, 3]:
  *   c[d] = sW * sum_{i in group} Wq_i * Vq_i[d]   (inner sum exact integer). */
 void add_group_quantized(const float* W, int i0, int n, const SeqView& sv, int D,
@@ -319,14 +360,16 @@ int orc_rope_rotate(int n, int D, float* x, const int32_t* positions, const floa
   return 0;
 }
 
-int orc_decode_head(int Hq, int Hkv, int D, int bs, int nb, int seq, int head,
-                    const int8_t* q_int8, const float* q_scale,
-                    const int8_t* k_cache, const int8_t* v_cache,
-                    const float* k_scale, const float* v_scale,
-                    const int32_t* block_tables, int max_blocks,
-                    const int32_t* seq_lens, int partition, int w_group,
-                    float softmax_scale, int flags, const orc_decode_trace* tr,
-                    float* out) {
+namespace {
+
+int decode_head_impl(int Hq, int Hkv, int D, int bs, int nb, int seq, int head,
+                     const int8_t* q_int8, const float* q_scale, const uint16_t* q_bf16,
+                     const int8_t* k_cache, const int8_t* v_cache,
+                     const float* k_scale, const float* v_scale,
+                     const int32_t* block_tables, int max_blocks,
+                     const int32_t* seq_lens, int partition, int w_group,
+                     float softmax_scale, int flags, const orc_decode_trace* tr,
+                     float* out) {
   if (!geometry_ok(Hq, Hkv, D, bs, nb) || w_group <= 0 || partition <= 0 ||
       partition % w_group != 0)
     return -1;
@@ -338,8 +381,9 @@ int orc_decode_head(int Hq, int Hkv, int D, int bs, int nb, int seq, int head,
   }
   Cache c{Hq, Hkv, D, bs, nb, k_cache, v_cache, k_scale, v_scale};
   SeqView sv{&c, block_tables + (size_t)seq * max_blocks, head / (Hq / Hkv)};
-  const int8_t* q = q_int8 + ((size_t)seq * Hq + head) * D;
-  const float sq = q_scale[(size_t)seq * Hq + head];
+  const size_t qr = (size_t)seq * Hq + head;
+  const Query q = q_bf16 ? Query{nullptr, 0.0f, q_bf16 + qr * D}
+                         : Query{q_int8 + qr * D, q_scale[qr], nullptr};
   const bool exact = (flags & ORC_EXACT) != 0;
   const bool bf16_pv = (flags & ORC_BF16_PV) != 0;
   const bool u8_w = (flags & ORC_UINT8_W) != 0;
@@ -349,9 +393,7 @@ int orc_decode_head(int Hq, int Hkv, int D, int bs, int nb, int seq, int head,
   std::vector<float> s(L);
   std::vector<double> s64(L);
   for (int i = 0; i < L; ++i) {
-    acc[i] = qk_acc(q, sv, i, D);
-    s[i] = score_f32(acc[i], sq, sv.sk(i), softmax_scale);
-    s64[i] = score_f64(acc[i], sq, sv.sk(i), softmax_scale);
+    q.score(sv, i, D, softmax_scale, &s[i], &s64[i], &acc[i]);
     if (tr && tr->acc) tr->acc[i] = acc[i];
     if (tr && tr->s) tr->s[i] = s[i];
   }
@@ -432,6 +474,37 @@ int orc_decode_head(int Hq, int Hkv, int D, int bs, int nb, int seq, int head,
   return 0;
 }
 
+int paged_decode_impl(int Hq, int Hkv, int D, int bs, int nb, int S, const int8_t* q_int8,
+                      const float* q_scale, const uint16_t* q_bf16, const int8_t* k_cache,
+                      const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                      const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
+                      int partition, int w_group, float softmax_scale, int flags, float* out) {
+  for (int b = 0; b < S; ++b)
+    for (int h = 0; h < Hq; ++h) {
+      int rc = decode_head_impl(Hq, Hkv, D, bs, nb, b, h, q_int8, q_scale, q_bf16, k_cache,
+                                v_cache, k_scale, v_scale, block_tables, max_blocks, seq_lens,
+                                partition, w_group, softmax_scale, flags, nullptr,
+                                out + ((size_t)b * Hq + h) * D);
+      if (rc) return rc;
+    }
+  return 0;
+}
+
+}  // namespace
+
+int orc_decode_head(int Hq, int Hkv, int D, int bs, int nb, int seq, int head,
+                    const int8_t* q_int8, const float* q_scale,
+                    const int8_t* k_cache, const int8_t* v_cache,
+                    const float* k_scale, const float* v_scale,
+                    const int32_t* block_tables, int max_blocks,
+                    const int32_t* seq_lens, int partition, int w_group,
+                    float softmax_scale, int flags, const orc_decode_trace* tr,
+                    float* out) {
+  return decode_head_impl(Hq, Hkv, D, bs, nb, seq, head, q_int8, q_scale, nullptr, k_cache,
+                          v_cache, k_scale, v_scale, block_tables, max_blocks, seq_lens,
+                          partition, w_group, softmax_scale, flags, tr, out);
+}
+
 int orc_paged_decode(int Hq, int Hkv, int D, int bs, int nb, int S,
                      const int8_t* q_int8, const float* q_scale,
                      const int8_t* k_cache, const int8_t* v_cache,
@@ -439,25 +512,34 @@ int orc_paged_decode(int Hq, int Hkv, int D, int bs, int nb, int S,
                      const int32_t* block_tables, int max_blocks,
                      const int32_t* seq_lens, int partition, int w_group,
                      float softmax_scale, int flags, float* out) {
-  for (int b = 0; b < S; ++b)
-    for (int h = 0; h < Hq; ++h) {
-      int rc = orc_decode_head(Hq, Hkv, D, bs, nb, b, h, q_int8, q_scale, k_cache,
-                               v_cache, k_scale, v_scale, block_tables, max_blocks,
-                               seq_lens, partition, w_group, softmax_scale, flags,
-                               nullptr, out + ((size_t)b * Hq + h) * D);
-      if (rc) return rc;
-    }
-  return 0;
+  return paged_decode_impl(Hq, Hkv, D, bs, nb, S, q_int8, q_scale, nullptr, k_cache, v_cache,
+                           k_scale, v_scale, block_tables, max_blocks, seq_lens, partition,
+                           w_group, softmax_scale, flags, out);
 }
 
-int orc_prefill_row(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
-                    int row, int head, const int8_t* q_int8,
-                    const float* q_scale, const int32_t* query_start_loc,
-                    const int32_t* seq_lens, const int8_t* k_cache,
-                    const int8_t* v_cache, const float* k_scale,
-                    const float* v_scale, const int32_t* block_tables,
-                    int max_blocks, int tile, int w_group, float softmax_scale,
-                    int flags, const orc_prefill_trace* tr, float* out) {
+int orc_paged_decode_bf16qk(int Hq, int Hkv, int D, int bs, int nb, int S,
+                            const uint16_t* q_bf16, const int8_t* k_cache,
+                            const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, int max_blocks,
+                            const int32_t* seq_lens, int partition, int w_group,
+                            float softmax_scale, int flags, float* out) {
+  if (!q_bf16) return -1;
+  return paged_decode_impl(Hq, Hkv, D, bs, nb, S, nullptr, nullptr, q_bf16, k_cache, v_cache,
+                           k_scale, v_scale, block_tables, max_blocks, seq_lens, partition,
+                           w_group, softmax_scale, flags, out);
+}
+
+namespace {
+
+int prefill_row_impl(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
+                     int row, int head, const int8_t* q_int8,
+                     const float* q_scale, const uint16_t* q_bf16,
+                     const int32_t* query_start_loc,
+                     const int32_t* seq_lens, const int8_t* k_cache,
+                     const int8_t* v_cache, const float* k_scale,
+                     const float* v_scale, const int32_t* block_tables,
+                     int max_blocks, int tile, int w_group, float softmax_scale,
+                     int flags, const orc_prefill_trace* tr, float* out) {
   if (!geometry_ok(Hq, Hkv, D, bs, nb) || w_group <= 0 || tile <= 0 ||
       tile % w_group != 0 || row < 0 || row >= Tq)
     return -1;
@@ -474,8 +556,9 @@ int orc_prefill_row(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
 
   Cache c{Hq, Hkv, D, bs, nb, k_cache, v_cache, k_scale, v_scale};
   SeqView sv{&c, block_tables + (size_t)b * max_blocks, head / (Hq / Hkv)};
-  const int8_t* q = q_int8 + ((size_t)row * Hq + head) * D;
-  const float sq = q_scale[(size_t)row * Hq + head];
+  const size_t qr = (size_t)row * Hq + head;
+  const Query q = q_bf16 ? Query{nullptr, 0.0f, q_bf16 + qr * D}
+                         : Query{q_int8 + qr * D, q_scale[qr], nullptr};
   const bool exact = (flags & ORC_EXACT) != 0;
   const bool bf16_pv = (flags & ORC_BF16_PV) != 0;
   const bool quant_w = (flags & ORC_NO_WQUANT) == 0 && !bf16_pv;
@@ -490,9 +573,8 @@ int orc_prefill_row(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
     std::vector<float> s(n);
     std::vector<double> s64(n);
     for (int j = 0; j < n; ++j) {
-      const int32_t a = qk_acc(q, sv, t0 + j, D);
-      s[j] = score_f32(a, sq, sv.sk(t0 + j), softmax_scale);
-      s64[j] = score_f64(a, sq, sv.sk(t0 + j), softmax_scale);
+      int32_t a;
+      q.score(sv, t0 + j, D, softmax_scale, &s[j], &s64[j], &a);
       if (tr && tr->s) tr->s[t0 + j] = s[j];
     }
     if (exact) {
@@ -550,6 +632,43 @@ int orc_prefill_row(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
   return 0;
 }
 
+int prefix_prefill_impl(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
+                        const int8_t* q_int8, const float* q_scale, const uint16_t* q_bf16,
+                        const int32_t* query_start_loc, const int32_t* seq_lens,
+                        const int8_t* k_cache, const int8_t* v_cache, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables, int max_blocks,
+                        int tile, int w_group, float softmax_scale, int flags,
+                        const int32_t* rows, int nrows, float* out) {
+  const int n = rows ? nrows : Tq;
+  for (int r = 0; r < n; ++r) {
+    const int row = rows ? rows[r] : r;
+    for (int h = 0; h < Hq; ++h) {
+      int rc = prefill_row_impl(Hq, Hkv, D, bs, nb, S, Tq, row, h, q_int8, q_scale, q_bf16,
+                                query_start_loc, seq_lens, k_cache, v_cache, k_scale, v_scale,
+                                block_tables, max_blocks, tile, w_group, softmax_scale, flags,
+                                nullptr, out + ((size_t)row * Hq + h) * D);
+      if (rc) return rc;
+    }
+  }
+  return 0;
+}
+
+}  // namespace
+
+int orc_prefill_row(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
+                    int row, int head, const int8_t* q_int8,
+                    const float* q_scale, const int32_t* query_start_loc,
+                    const int32_t* seq_lens, const int8_t* k_cache,
+                    const int8_t* v_cache, const float* k_scale,
+                    const float* v_scale, const int32_t* block_tables,
+                    int max_blocks, int tile, int w_group, float softmax_scale,
+                    int flags, const orc_prefill_trace* tr, float* out) {
+  return prefill_row_impl(Hq, Hkv, D, bs, nb, S, Tq, row, head, q_int8, q_scale, nullptr,
+                          query_start_loc, seq_lens, k_cache, v_cache, k_scale, v_scale,
+                          block_tables, max_blocks, tile, w_group, softmax_scale, flags, tr,
+                          out);
+}
+
 int orc_prefix_prefill(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
                        const int8_t* q_int8, const float* q_scale,
                        const int32_t* query_start_loc, const int32_t* seq_lens,
@@ -558,19 +677,24 @@ int orc_prefix_prefill(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
                        const int32_t* block_tables, int max_blocks, int tile,
                        int w_group, float softmax_scale, int flags,
                        const int32_t* rows, int nrows, float* out) {
-  const int n = rows ? nrows : Tq;
-  for (int r = 0; r < n; ++r) {
-    const int row = rows ? rows[r] : r;
-    for (int h = 0; h < Hq; ++h) {
-      int rc = orc_prefill_row(Hq, Hkv, D, bs, nb, S, Tq, row, h, q_int8, q_scale,
-                               query_start_loc, seq_lens, k_cache, v_cache, k_scale,
-                               v_scale, block_tables, max_blocks, tile, w_group,
-                               softmax_scale, flags, nullptr,
-                               out + ((size_t)row * Hq + h) * D);
-      if (rc) return rc;
-    }
-  }
-  return 0;
+  return prefix_prefill_impl(Hq, Hkv, D, bs, nb, S, Tq, q_int8, q_scale, nullptr,
+                             query_start_loc, seq_lens, k_cache, v_cache, k_scale, v_scale,
+                             block_tables, max_blocks, tile, w_group, softmax_scale, flags, rows,
+                             nrows, out);
+}
+
+int orc_prefix_prefill_bf16qk(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
+                              const uint16_t* q_bf16, const int32_t* query_start_loc,
+                              const int32_t* seq_lens, const int8_t* k_cache,
+                              const int8_t* v_cache, const float* k_scale,
+                              const float* v_scale, const int32_t* block_tables,
+                              int max_blocks, int tile, int w_group, float softmax_scale,
+                              int flags, const int32_t* rows, int nrows, float* out) {
+  if (!q_bf16) return -1;
+  return prefix_prefill_impl(Hq, Hkv, D, bs, nb, S, Tq, nullptr, nullptr, q_bf16,
+                             query_start_loc, seq_lens, k_cache, v_cache, k_scale, v_scale,
+                             block_tables, max_blocks, tile, w_group, softmax_scale, flags, rows,
+                             nrows, out);
 }
 
 }  // extern "C"

@@ -126,6 +126,18 @@ int orc_paged_decode(int Hq, int Hkv, int D, int bs, int nb, int S,
                      const int32_t* seq_lens, int partition, int w_group,
                      float softmax_scale, int flags, float* out);
 
+/* BF16-QK ablation of orc_paged_decode: the query is q_bf16 [S, Hq, D] (bf16
+ * bits, not quantized) against the int8 K codes; score = ((float)dot * sK) *
+ * softmax_scale with dot = sum_d q[d] * k8[d] summed in fp64 and rounded once
+ * to fp32 (fp64 throughout under ORC_EXACT).  Everything after the scores is
+ * orc_paged_decode's, flags included. */
+int orc_paged_decode_bf16qk(int Hq, int Hkv, int D, int bs, int nb, int S,
+                            const uint16_t* q_bf16, const int8_t* k_cache,
+                            const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                            const int32_t* block_tables, int max_blocks,
+                            const int32_t* seq_lens, int partition, int w_group,
+                            float softmax_scale, int flags, float* out);
+
 /* Same computation for one (seq, q head), filling `trace`; out [D]. */
 int orc_decode_head(int Hq, int Hkv, int D, int bs, int nb, int seq, int head,
                     const int8_t* q_int8, const float* q_scale,
@@ -170,6 +182,16 @@ int orc_prefill_row(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
                     const float* v_scale, const int32_t* block_tables,
                     int max_blocks, int tile, int w_group, float softmax_scale,
                     int flags, const orc_prefill_trace* trace, float* out);
+
+/* BF16-QK ablation of orc_prefix_prefill: q_bf16 [Tq, Hq, D] bf16 bits, scores
+ * as in orc_paged_decode_bf16qk, the rest unchanged. */
+int orc_prefix_prefill_bf16qk(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
+                              const uint16_t* q_bf16, const int32_t* query_start_loc,
+                              const int32_t* seq_lens, const int8_t* k_cache,
+                              const int8_t* v_cache, const float* k_scale,
+                              const float* v_scale, const int32_t* block_tables,
+                              int max_blocks, int tile, int w_group, float softmax_scale,
+                              int flags, const int32_t* rows, int nrows, float* out);
 
 /* Correctly rounded fp32 exponential used by the oracle. */
 float orc_expf(float x);

@@ -25,6 +25,9 @@ when the oracle disagrees with what the pages or the mathematics fix:
 * the BF16-PV ablation (decode and prefill): W rounded to bf16 exactly as
   torch rounds it, the partition sums / the tile re-assembly recomputed, and
   the bound against unquantized attention;
+* the BF16-QK ablation (decode and prefill): bit-identical to the int8 path
+  for a bf16 query that is int8 codes times a power of two, exact mode
+  against numpy softmax attention of the bf16 query, and the decode bound;
 * the rotary embedding against complex multiplication in fp64 (within the
   rounding of two fp32 products and a sum), exact quarter turns and identity
   tables, relative-position invariance of dot products; the producer with
@@ -860,9 +863,102 @@ def pin_prefill_vs_decode(orc, G=32, seed=9):
     return worst
 
 
+def _q_bf16_from_codes(q8, shift=6):
+    """bf16 bits of q8 * 2^-shift: exact, since |q8| <= 127 needs 7 bits."""
+    return W.f32_to_bf16_bits(q8.astype(np.float32) * np.float32(2.0 ** -shift))
+
+
+def pin_decode_bf16_qk(orc, G=32, seed=18):
+    """The BF16-QK ablation (decode).
+    (1) A bf16 query equal to int8 codes times 2^-6 must give, bit for bit,
+        the int8 path's output with q_scale = 2^-6 (the dot product is then
+        acc * sQ exactly, and the rest is shared).
+    (2) Exact mode: softmax attention of the bf16 query over the dequantized
+        cache, written here with numpy in fp64.
+    (3) With the W groups, one partition: within the a-priori bound against
+        unquantized fp64 attention -- the QK term from the bf16 query's own
+        probabilities (no Q quantization), plus |eV| <= sV/2 and
+        |eW| <= sW/2 with sW = max P sV / 127 per group."""
+    wl = tiny_decode(seed=seed, seq_lens=(1, 9, 40, 256, 300, 600))
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    grp = wl.num_q_heads // wl.num_kv_heads
+    tables = (cache, wl.block_tables, wl.seq_lens)
+    # (1)
+    qb = _q_bf16_from_codes(q8)
+    for flags in (0, ORC_NO_WQUANT):
+        o8 = orc.paged_decode(q8, np.full_like(qs, 2.0 ** -6), *tables,
+                              num_q_heads=wl.num_q_heads, w_group=G, flags=flags)
+        ob = orc.paged_decode_bf16qk(qb, *tables, w_group=G, flags=flags)
+        assert np.array_equal(o8, ob), "bf16-QK with q = codes * 2^-6 != int8 path"
+    # (2) and (3): the workload's own bf16 queries
+    qrows = wl.decode_query_rows()
+    qreal = wl.query[qrows]
+    ex = orc.paged_decode_bf16qk(qreal, *tables, w_group=G, flags=ORC_EXACT | ORC_NO_WQUANT)
+    ref = decode_reference_fp64(wl)
+    for b in range(wl.num_seqs):
+        L = int(wl.seq_lens[b])
+        sl = seq_slots(wl, b)
+        big = 256 * -(-L // 256)
+        ob = orc.paged_decode_bf16qk(qreal[b:b + 1], cache, wl.block_tables[b:b + 1],
+                                     wl.seq_lens[b:b + 1], w_group=G, partition=big)[0]
+        tok = np.nonzero(wl.token_seq == b)[0]
+        tok = tok[np.argsort(wl.token_pos[tok])]
+        for h in range(wl.num_q_heads):
+            kv = h // grp
+            qf = W.bf16_bits_to_f32(qreal[b, h]).astype(np.float64)
+            kdq = K[sl, kv].astype(np.float64) * sK[sl, kv].astype(np.float64)[:, None]
+            sVt = sV[sl, kv].astype(np.float64)
+            vq = V[sl, kv].astype(np.float64)
+            p = _softmax64(kdq @ qf * wl.softmax_scale)
+            want = (p * sVt) @ vq
+            assert np.all(np.abs(ex[b, h] - want) <= 1e-6 * (np.abs(want) + 1e-3)), \
+                f"exact bf16-QK decode seq {b} head {h} != softmax over the dequantized cache"
+            Vorig = W.bf16_bits_to_f32(wl.value[tok, kv]).astype(np.float64)
+            Korig = W.bf16_bits_to_f32(wl.key[tok, kv]).astype(np.float64)
+            Pe = _softmax64(Korig @ qf / np.sqrt(wl.head_dim))
+            wmax = np.array([(p[g:g + G] * sVt[g:g + G]).max() for g in range(0, L, G)])
+            sWt = np.repeat(wmax / 127 * (1 + 1e-5), G)[:L]
+            bound = (np.abs(Pe - p) @ np.abs(Vorig) + (p * sVt / 2).sum()
+                     + (sWt / 2) @ np.abs(vq)) * (1 + 1e-4) + 1e-6
+            err = np.abs(ob[h] - ref[b, h])
+            assert np.all(err <= bound), f"bf16-QK decode seq {b} head {h}: error above bound"
+
+
+def pin_prefill_bf16_qk(orc, G=32, seed=19):
+    """The BF16-QK ablation (prefill): (1) bit for bit the int8 path when the
+    bf16 query is int8 codes times 2^-6 and q_scale = 2^-6, for two tile
+    sizes; (2) exact mode equals causal softmax attention of the bf16 query
+    over the dequantized cache, written here with numpy in fp64."""
+    wl = tiny_prefill(seed=seed)
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    grp = wl.num_q_heads // wl.num_kv_heads
+    loc = (wl.query_start_loc, wl.seq_lens, cache, wl.block_tables)
+    qb = _q_bf16_from_codes(q8)
+    for tile in (256, 64):
+        o8 = orc.prefix_prefill(q8, np.full_like(qs, 2.0 ** -6), *loc, w_group=G, tile=tile)
+        ob = orc.prefix_prefill_bf16qk(qb, *loc, w_group=G, tile=tile)
+        assert np.array_equal(o8, ob), "bf16-QK prefill with q = codes * 2^-6 != int8 path"
+    qreal = wl.query  # [Tq, Hq, D]: the chunk's bf16 queries, row for row
+    ex = orc.prefix_prefill_bf16qk(qreal, *loc, w_group=G, tile=64,
+                                   flags=ORC_EXACT | ORC_NO_WQUANT)
+    for r, b, pos in _prefill_rows(wl):
+        sl = seq_slots(wl, b)[:pos + 1]
+        for h in range(wl.num_q_heads):
+            kv = h // grp
+            qf = W.bf16_bits_to_f32(qreal[r, h]).astype(np.float64)
+            kdq = K[sl, kv].astype(np.float64) * sK[sl, kv].astype(np.float64)[:, None]
+            p = _softmax64(kdq @ qf * wl.softmax_scale)
+            want = (p * sV[sl, kv].astype(np.float64)) @ V[sl, kv].astype(np.float64)
+            assert np.all(np.abs(ex[r, h] - want) <= 1e-6 * (np.abs(want) + 1e-3)), \
+                f"exact bf16-QK prefill row {r} head {h} != causal softmax"
+
+
 ALL_PINS = [pin_quantize_golden, pin_quantize_bruteforce, pin_cache_layout,
             pin_decode_trace, pin_decode_bruteforce, pin_decode_partition_invariance,
             pin_decode_special_cases, pin_prefill_exact, pin_prefill_trace,
             pin_prefill_vs_decode, pin_rope_rotation, pin_rope_producer,
             pin_bf16_rounding, pin_decode_bf16_pv, pin_quantize_w_u8, pin_decode_uint8_w,
-            pin_decode_multi_query, pin_prefill_bf16_pv]
+            pin_decode_multi_query, pin_prefill_bf16_pv, pin_decode_bf16_qk,
+            pin_prefill_bf16_qk]

@@ -93,6 +93,18 @@ MUTANTS = {
                             "x[d] = bf16_to_float(vs[d]);\n      if (cs) rope_rotate(x.data(), R, cs);\n")],
     "rope_position_off_by_one": [("cos_sin + (size_t)positions[t] * R",
                                   "cos_sin + (size_t)(positions[t] > 0 ? positions[t] - 1 : 1) * R")],
+    "bf16qk_k_unsigned": [("acc += (double)bf16_to_float(q[d]) * (double)sv.kq(i, d);",
+                           "acc += (double)bf16_to_float(q[d]) * (double)(uint8_t)sv.kq(i, d);")],
+    "bf16qk_query_truncated": [("acc += (double)bf16_to_float(q[d]) * (double)sv.kq(i, d);",
+                                "acc += (double)(int)bf16_to_float(q[d]) * (double)sv.kq(i, d);")],
+    "bf16qk_dims_reversed": [("acc += (double)bf16_to_float(q[d]) * (double)sv.kq(i, d);",
+                              "acc += (double)bf16_to_float(q[D - 1 - d]) * (double)sv.kq(i, d);")],
+    "bf16qk_first_head_query": [("Query{nullptr, 0.0f, q_bf16 + qr * D}",
+                                 "Query{nullptr, 0.0f, q_bf16 + qr / Hq * Hq * D}")],
+    "bf16qk_score_drops_sk": [("  float s = (float)dot;\n  s = s * sk;\n",
+                               "  float s = (float)dot;\n  (void)sk;\n")],
+    "bf16qk_exact_drops_sk": [("*s64 = dot * (double)sv.sk(i) * (double)softmax_scale;",
+                               "*s64 = dot * (double)softmax_scale;")],
     "rope_after_quantize": [(
         "      if (cs) rope_rotate(x.data(), R, cs);\n      orc_quantize(x.data(), D, q.data(), &s);\n"
         "      for (int d = 0; d < D; ++d) k_cache",
