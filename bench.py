@@ -311,8 +311,10 @@ def time_pv_ablation(L, G=32, steps=50, min_rotation_mb=512.0):
     group-quantized, int8 MFMA) and with a bf16 PV (W = P*sV in bf16, int8 V
     exact in bf16, bf16 MFMA), nothing else changed; a batch-1 decode at
     L tokens, 24 q / 4 KV heads x 256, 1% of V channels x20; the UINT8-W
-    variant is timed beside them.  Returns us per call of each and the
-    speed-up of the int8 PV (bf16 us / int8 us)."""
+    variant and the QK comparison (the bf16 query against the int8 K on the
+    bf16 matrix unit) are timed beside them.  Returns us per call of each and
+    the speed-ups of the int8 PV (bf16 PV us / int8 us) and of the int8 QK
+    (bf16 QK us / int8 us)."""
     import numpy as np
     import torch
 
@@ -334,6 +336,7 @@ def time_pv_ablation(L, G=32, steps=50, min_rotation_mb=512.0):
                                     base.k_scale.clone(), base.v_scale.clone())
                        for _ in range(copies - 1)]
     bt, sl = dev(wl.block_tables), dev(wl.seq_lens)
+    qb = dev(np.ascontiguousarray(wl.query[wl.decode_query_rows()]).view(np.int16))
     ws = torch.zeros(K.paged_decode_workspace_bytes(d, wl.num_seqs, wl.max_seq_len),
                      dtype=torch.uint8, device="cuda")
     out = torch.empty((wl.num_seqs, d.num_q_heads, d.head_dim), dtype=torch.float32,
@@ -344,6 +347,9 @@ def time_pv_ablation(L, G=32, steps=50, min_rotation_mb=512.0):
         "bf16": lambda i: K.paged_decode_bf16pv(d, q8, qs, caches[i % copies], bt, sl,
                                                 wl.max_seq_len, workspace=ws, out=out),
         "uint8w": lambda i: K.paged_decode_uint8w(d, q8, qs, caches[i % copies], bt, sl,
+                                                  wl.max_seq_len, w_group=G, workspace=ws,
+                                                  out=out),
+        "bf16qk": lambda i: K.paged_decode_bf16qk(d, qb, caches[i % copies], bt, sl,
                                                   wl.max_seq_len, w_group=G, workspace=ws,
                                                   out=out),
     }
@@ -366,8 +372,10 @@ def time_pv_ablation(L, G=32, steps=50, min_rotation_mb=512.0):
             e1.record()
             torch.cuda.synchronize()
             runs.append(1e3 * e0.elapsed_time(e1) / steps)
-        res[f"{name}_us" if name == "uint8w" else f"{name}_pv_us"] = round(float(np.median(runs)), 3)
+        key = f"{name}_us" if name in ("uint8w", "bf16qk") else f"{name}_pv_us"
+        res[key] = round(float(np.median(runs)), 3)
     res["int8_pv_speedup"] = round(res["bf16_pv_us"] / res["int8_pv_us"], 4)
+    res["int8_qk_speedup"] = round(res["bf16qk_us"] / res["int8_pv_us"], 4)
     return res
 
 

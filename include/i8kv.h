@@ -1,7 +1,7 @@
 /*
  * i8kv -- paged attention over an INT8 KV cache, native to AMD MI355X (gfx950).
  *
- * C ABI of the library libi8kv.so.  Nine calls, on the operations defined on the pages
+ * C ABI of the library libi8kv.so.  Ten calls, on the operations defined on the pages
  *   [KV] "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
  *        DCU" (part 1 of the series), and
  *   [PV] "Implementing INT8 PV MMAC on a gfx936 DCU: V-scale fusion,
@@ -23,6 +23,8 @@
  *   i8kv_paged_decode_ex    -- the decode with options: PV variant, several
  *                              causal queries per sequence, bf16 output
  *   i8kv_prefix_prefill_bf16pv -- the prefill with a bf16 PV product ([PV] 5)
+ *   i8kv_paged_decode_bf16qk -- the decode with a bf16 QK product (the
+ *                              pages' QK comparison, [KV] 4.1)
  *
  * Conventions for every call
  *  - Tensor arguments are DEVICE pointers owned by the caller, C-contiguous in
@@ -189,6 +191,27 @@ i8kv_status i8kv_paged_decode_bf16pv(const i8kv_cache_desc* desc, int32_t num_se
                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                                      const int32_t* seq_lens, int32_t max_seq_len,
                                      int32_t partition_size, float softmax_scale, void* workspace,
+                                     size_t workspace_bytes, float* out, i8kv_stream_t stream);
+
+/*
+ * The BF16-QK ablation of i8kv_paged_decode_int8 ([KV] 4.1 compares the int8
+ * QK matrix block with a bf16 one): the query is not quantized; its bf16
+ * values meet the int8 K codes, taken exactly as bf16, in
+ * v_mfma_f32_16x16x32_bf16 with fp32 accumulation, and
+ *   score_i = (dot_i * sK_i) * softmax_scale,   dot_i = sum_d q[d] * Kq_i[d].
+ * Partitions, softmax, the int8 W groups, PV and the merge are those of
+ * i8kv_paged_decode_int8.
+ *   query_bf16 [S, Hq, D] bf16 bits (16-byte aligned) in place of q_int8 and
+ *   q_scale; every other argument, the workspace size and the errors as
+ *   i8kv_paged_decode_int8.
+ */
+i8kv_status i8kv_paged_decode_bf16qk(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                     const uint16_t* query_bf16, const int8_t* k_cache,
+                                     const int8_t* v_cache, const float* k_scale,
+                                     const float* v_scale, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                     int32_t max_seq_len, int32_t partition_size,
+                                     int32_t w_group, float softmax_scale, void* workspace,
                                      size_t workspace_bytes, float* out, i8kv_stream_t stream);
 
 /*

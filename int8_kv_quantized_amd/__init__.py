@@ -12,6 +12,7 @@ fails loudly if the library has not been built -- there is no fallback.
     paged_decode_workspace_bytes(desc, num_seqs, max_seq_len)
     paged_decode_int8(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
     paged_decode_bf16pv(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
+    paged_decode_bf16qk(desc, query, cache, block_tables, seq_lens, ...)
     paged_decode_uint8w(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
     paged_decode_ex(desc, q_int8, q_scale, cache, block_tables, seq_lens, max_seq_len,
                     queries_per_seq=1, pv="int8", w_group=32, out_bf16=False, ...)
@@ -33,6 +34,7 @@ from ._binding import (  # noqa: F401
     lib_path,
     load_library,
     paged_decode_bf16pv,
+    paged_decode_bf16qk,
     paged_decode_ex,
     paged_decode_ex_workspace_bytes,
     paged_decode_int8,

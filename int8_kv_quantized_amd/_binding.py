@@ -92,6 +92,9 @@ def load_library():
     lib.i8kv_paged_decode_ex.argtypes = ([D, O, I32] + [P] * 7 + [I32, P, I32, P, SZ, P, P])
     lib.i8kv_paged_decode_bf16pv.restype = C.c_int
     lib.i8kv_paged_decode_bf16pv.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, F, P, SZ, P, P])
+    lib.i8kv_paged_decode_bf16qk.restype = C.c_int
+    lib.i8kv_paged_decode_bf16qk.argtypes = ([D, I32] + [P] * 6 + [I32, P, I32, I32, I32, F, P, SZ,
+                                                                  P, P])
     lib.i8kv_decode_step_int8.restype = C.c_int
     lib.i8kv_decode_step_int8.argtypes = ([D, I32] + [P] * 10 + [I32, P, I32, I32, I32, F, P, SZ,
                                                                   P, P])
@@ -278,12 +281,16 @@ def paged_decode_workspace_bytes(desc: CacheDesc, num_seqs: int, max_seq_len: in
 
 
 def _decode_args(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables, seq_lens,
-                 max_seq_len, partition_size, softmax_scale, workspace, out):
+                 max_seq_len, partition_size, softmax_scale, workspace, out, q_bf16=None):
     import torch
-    S = int(seq_lens.shape[0]) if _is_tensor(seq_lens) else int(q_int8.shape[0])
+    q_any = q_int8 if q_bf16 is None else q_bf16
+    S = int(seq_lens.shape[0]) if _is_tensor(seq_lens) else int(q_any.shape[0])
     Hq, D = desc.num_q_heads, desc.head_dim
-    _check(q_int8, "q_int8", torch.int8, (S, Hq, D))
-    _check(q_scale, "q_scale", torch.float32, (S, Hq))
+    if q_bf16 is None:
+        _check(q_int8, "q_int8", torch.int8, (S, Hq, D))
+        _check(q_scale, "q_scale", torch.float32, (S, Hq))
+    else:
+        _check(q_bf16, "query", (torch.bfloat16, torch.int16, torch.uint16), (S, Hq, D))
     cache.check(desc)
     _check(block_tables, "block_tables", torch.int32)
     if not _is_tensor(block_tables):
@@ -409,6 +416,26 @@ def paged_decode_bf16pv(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, blo
         int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(partition_size),
         scale, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
     _raise("paged_decode_bf16pv", st)
+    return out
+
+
+def paged_decode_bf16qk(desc: CacheDesc, query, cache: PagedCache, block_tables, seq_lens,
+                        max_seq_len: int, w_group: int = 32, partition_size: int = 256,
+                        softmax_scale: Optional[float] = None, workspace=None, out=None,
+                        stream=None):
+    """The BF16-QK ablation of paged_decode_int8: ``query`` [S, Hq, D] bf16
+    (torch.bfloat16, or its bits as int16 / uint16), not quantized, against
+    the int8 K codes; the other arguments as paged_decode_int8."""
+    lib = load_library()
+    S, scale, workspace, ws_bytes, out = _decode_args(
+        desc, None, None, cache, block_tables, seq_lens, max_seq_len, partition_size,
+        softmax_scale, workspace, out, q_bf16=query)
+    st = lib.i8kv_paged_decode_bf16qk(
+        C.byref(desc), S, _ptr(query), _ptr(cache.k_cache), _ptr(cache.v_cache),
+        _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(partition_size),
+        int(w_group), scale, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
+    _raise("paged_decode_bf16qk", st)
     return out
 
 

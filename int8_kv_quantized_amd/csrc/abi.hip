@@ -203,13 +203,14 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
                        int32_t partition_size, int32_t w_group, float softmax_scale,
                        void* workspace, size_t workspace_bytes, float* out,
                        const DecodeArgs* fused, i8kv_stream_t stream, bool pv_bf16 = false,
-                       bool w_uint8 = false, int32_t nq = 1, uint16_t* out16 = nullptr) {
+                       bool w_uint8 = false, int32_t nq = 1, uint16_t* out16 = nullptr,
+                       const uint16_t* q_bf16 = nullptr) {
   i8kv_status st = check_desc(desc);
   if (st != I8KV_OK) return st;
   if (!k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !seq_lens ||
       (!out && !out16))
     return I8KV_ERR_NULL;
-  if (!fused && (!q_int8 || !q_scale)) return I8KV_ERR_NULL;
+  if (!fused && !q_bf16 && (!q_int8 || !q_scale)) return I8KV_ERR_NULL;
   if (fused && (!fused->new_key || !fused->new_value || !fused->new_query)) return I8KV_ERR_NULL;
   if (fused && (!q_int8) != (!q_scale)) return I8KV_ERR_NULL;
   if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq <= 0) return I8KV_ERR_INVALID_ARG;
@@ -222,7 +223,8 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
       (int64_t)nq * desc->num_q_heads > 0x7fffffff)
     return I8KV_ERR_UNSUPPORTED;
   if (max_seq_len > kMaxSeqLen || num_seqs > kMaxGridYZ) return I8KV_ERR_UNSUPPORTED;
-  if ((q_int8 && !aligned16(q_int8)) || !aligned16(k_cache) || !aligned16(v_cache) ||
+  if ((q_int8 && !aligned16(q_int8)) || (q_bf16 && !aligned16(q_bf16)) ||
+      !aligned16(k_cache) || !aligned16(v_cache) ||
       (out && !aligned16(out)) || (out16 && !aligned16(out16)))
     return I8KV_ERR_INVALID_ARG;
   if (fused && (!aligned16(fused->new_key) || !aligned16(fused->new_value) ||
@@ -251,8 +253,9 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
   a.w_uint8 = w_uint8 ? 1 : 0;
   a.nq = nq;
   a.softmax_scale = softmax_scale;
-  a.q_int8 = fused ? nullptr : q_int8;
-  a.q_scale = fused ? nullptr : q_scale;
+  a.q_int8 = fused || q_bf16 ? nullptr : q_int8;
+  a.q_scale = fused || q_bf16 ? nullptr : q_scale;
+  a.q_bf16 = fused ? nullptr : q_bf16;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.k_scale = k_scale;
@@ -313,6 +316,21 @@ i8kv_status i8kv_paged_decode_uint8w(const i8kv_cache_desc* desc, int32_t num_se
                     block_tables, max_blocks_per_seq, seq_lens, max_seq_len, partition_size,
                     w_group, softmax_scale, workspace, workspace_bytes, out, nullptr, stream,
                     /*pv_bf16=*/false, /*w_uint8=*/true);
+}
+
+i8kv_status i8kv_paged_decode_bf16qk(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                     const uint16_t* query_bf16, const int8_t* k_cache,
+                                     const int8_t* v_cache, const float* k_scale,
+                                     const float* v_scale, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                     int32_t max_seq_len, int32_t partition_size,
+                                     int32_t w_group, float softmax_scale, void* workspace,
+                                     size_t workspace_bytes, float* out, i8kv_stream_t stream) {
+  if (!query_bf16) return I8KV_ERR_NULL;
+  return run_decode(desc, num_seqs, nullptr, nullptr, k_cache, v_cache, k_scale, v_scale,
+                    block_tables, max_blocks_per_seq, seq_lens, max_seq_len, partition_size,
+                    w_group, softmax_scale, workspace, workspace_bytes, out, nullptr, stream,
+                    /*pv_bf16=*/false, /*w_uint8=*/false, /*nq=*/1, /*out16=*/nullptr, query_bf16);
 }
 
 size_t i8kv_paged_decode_ex_workspace_bytes(const i8kv_cache_desc* desc,

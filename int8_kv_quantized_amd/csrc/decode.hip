@@ -82,7 +82,10 @@ struct DecodeShape {
 // bf16), and UINT8 W groups (codes 0..255 against max W / 255).
 enum : int { kPvInt8 = 0, kPvBf16 = 1, kPvUint8 = 2 };
 
-template <int D, int G, bool FUSED, int PVM, bool MQ>
+// QB: the BF16-QK ablation -- the bf16 queries (not quantized) against the
+// int8 K codes taken exactly as bf16, v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation, score = (dot * sK) * softmax_scale; the rest is unchanged.
+template <int D, int G, bool FUSED, int PVM, bool MQ, bool QB>
 __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_partition_kernel(
     DecodeArgs a) {
   constexpr bool BPV = PVM == kPvBf16;
@@ -137,6 +140,7 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   for (int g = 0; g < 4; ++g) pidv[g] = bt_at(4 * g + lg);      // V pages of this lane
   int pids = bt_at(tsv >> 4);
   v4i qa[NC];
+  v4u qh[QB ? NC : 1][2];  // QB: bf16 dims 64c + 16lg + 8e .. +7 of row lr
   float sq[4];
   // Fused step: wave w quantizes items w, w + NW, ... of the group's grp q
   // heads followed by the newest token's K (item grp) and V (item grp + 1);
@@ -155,6 +159,18 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
         raw[k] = load_wave_vector<D>(
             (it == grp ? a.new_key : a.new_value) + ((size_t)s * Hkv + kv) * D, lane);
     }
+  } else if constexpr (QB) {
+    const bool vh = lr < rows;
+    const uint16_t* qp = a.q_bf16 + qrow(vh ? lr : 0) * D + 16 * lg;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        qh[c][e] = *reinterpret_cast<const v4u*>(qp + 64 * c + 8 * e);
+        if (!vh) qh[c][e] = v4u{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sq[r] = 1.0f;
   } else {
     const bool vh = lr < rows;
     const int8_t* qp = a.q_int8 + qrow(vh ? lr : 0) * D + 16 * lg;
@@ -296,12 +312,27 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
 
   // ---- QK, the V loads, then scores -> LDS -------------------------------------
   v4i qk[PPW];
+  v4f qkf[QB ? PPW : 1];
 #pragma unroll
   for (int j = 0; j < PPW; ++j) {
-    qk[j] = v4i{0, 0, 0, 0};
+    if constexpr (QB) {
+      // the lane's 16 K bytes of chunk 4c + lg are dims 64c + 16lg .. +15: two
+      // bf16 k-slices of 8, matched by the query halves qh[c][0], qh[c][1]
+      qkf[j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qk[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[c], kb[j][c], qk[j], 0, 0, 0);
+      for (int c = 0; c < NC; ++c) {
+        const v4u kw = __builtin_bit_cast(v4u, kb[j][c]);
+        qkf[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(v8bf, qh[c][0]), i8x8_to_bf16(kw[0], kw[1]), qkf[j], 0, 0, 0);
+        qkf[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(v8bf, qh[c][1]), i8x8_to_bf16(kw[2], kw[3]), qkf[j], 0, 0, 0);
+      }
+    } else {
+      qk[j] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        qk[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[c], kb[j][c], qk[j], 0, 0, 0);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   v4i vb[4][NCW];
@@ -320,7 +351,7 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * lg + r;
       if (h < rows) {
-        float x = (float)qk[j][r] * sq[r];
+        float x = QB ? qkf[j][r] : (float)qk[j][r] * sq[r];
         x = x * sk[j];
         x = x * a.softmax_scale;
         // causal: query qi sits at position L - nq + qi and sees keys up to it
@@ -604,34 +635,37 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
   dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
   dim3 mgrid((unsigned)(a.num_q_heads * a.nq), (unsigned)a.num_seqs, (unsigned)(a.head_dim / 64));
-#define I8KV_DECODE_CASE(DD, GG)                                                             \
-  if (a.head_dim == DD && (a.pv_bf16 ? GG == 64 : a.w_group == GG)) {                       \
-    const dim3 blk(DecodeShape<DD>::NW * kWave);                                             \
-    const bool mq = a.nq > 1;                                                                \
-    if (a.new_key)                                                                           \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8, false>), grid,\
-                         blk, 0, stream, a);                                                 \
-    else if (a.pv_bf16 && mq)                                                                \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvBf16, true>), grid,\
-                         blk, 0, stream, a);                                                 \
-    else if (a.pv_bf16)                                                                      \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvBf16, false>),     \
-                         grid, blk, 0, stream, a);                                           \
-    else if (a.w_uint8 && mq)                                                                \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvUint8, true>),     \
-                         grid, blk, 0, stream, a);                                           \
-    else if (a.w_uint8)                                                                      \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvUint8, false>),    \
-                         grid, blk, 0, stream, a);                                           \
-    else if (mq)                                                                             \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, true>), grid,\
-                         blk, 0, stream, a);                                                 \
-    else                                                                                     \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false>),     \
-                         grid, blk, 0, stream, a);                                           \
-    if (a.max_parts > 1)                                                                     \
-      hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(kWave), 0, stream, a); \
-    return hipGetLastError();                                                                \
+#define I8KV_DECODE_CASE(DD, GG)                                                                 \
+  if (a.head_dim == DD && (a.pv_bf16 ? GG == 64 : a.w_group == GG)) {                            \
+    const dim3 blk(DecodeShape<DD>::NW * kWave);                                                 \
+    const bool mq = a.nq > 1;                                                                    \
+    if (a.new_key)                                                                               \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8, false, false>),   \
+                         grid, blk, 0, stream, a);                                               \
+    else if (a.q_bf16)                                                                           \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false, true>),   \
+                         grid, blk, 0, stream, a);                                               \
+    else if (a.pv_bf16 && mq)                                                                    \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvBf16, true, false>),   \
+                         grid, blk, 0, stream, a);                                               \
+    else if (a.pv_bf16)                                                                          \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvBf16, false, false>),  \
+                         grid, blk, 0, stream, a);                                               \
+    else if (a.w_uint8 && mq)                                                                    \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvUint8, true, false>),  \
+                         grid, blk, 0, stream, a);                                               \
+    else if (a.w_uint8)                                                                          \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvUint8, false, false>), \
+                         grid, blk, 0, stream, a);                                               \
+    else if (mq)                                                                                 \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, true, false>),   \
+                         grid, blk, 0, stream, a);                                               \
+    else                                                                                         \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false, false>),  \
+                         grid, blk, 0, stream, a);                                               \
+    if (a.max_parts > 1)                                                                         \
+      hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(kWave), 0, stream, a);     \
+    return hipGetLastError();                                                                    \
   }
   I8KV_DECODE_CASE(64, 32)
   I8KV_DECODE_CASE(64, 64)

@@ -50,6 +50,7 @@ struct DecodeArgs {
   float softmax_scale;
   const int8_t* q_int8;
   const float* q_scale;
+  const uint16_t* q_bf16;  // the BF16-QK ablation: bf16 queries [S, Hq, D] instead
   const int8_t* k_cache;
   const int8_t* v_cache;
   const float* k_scale;
@@ -84,6 +85,7 @@ struct PrefillArgs {
   float softmax_scale;
   const int8_t* q_int8;
   const float* q_scale;
+  const uint16_t* q_bf16;  // the BF16-QK ablation: bf16 queries [Tq, Hq, D] instead
   const int32_t* query_start_loc;
   const int32_t* seq_lens;
   const int8_t* k_cache;

@@ -103,8 +103,8 @@ double score_f64(int32_t acc, float sq, float sk, float softmax_scale) {
   return (double)acc * (double)sq * (double)sk * (double)softmax_scale;
 }
 
-/* BF16-QK ablation (the QK half of the comparison at the matrix-block
- * boundary [KV 4]; [PV 5] switches the PV half): the query is not quantized
+/* BF16-QK ablation (the QK row of the operator-level comparison [KV 4.1];
+ * [PV 5] switches the PV half): the query is not quantized
  * and its bf16 values meet the int8 K codes exactly.  Each product has at
  * most 16 significant bits, the sum over d is taken in fp64 and rounded once
  * to fp32, and the score is (dot * sK) * softmax_scale in fp32, the int8

@@ -27,7 +27,8 @@ def test_header_declares_the_operations():
     names = declared_functions()
     for op in ("i8kv_kv_quantize_write", "i8kv_kv_quantize_write_rope", "i8kv_paged_decode_int8",
                "i8kv_paged_decode_bf16pv", "i8kv_paged_decode_uint8w", "i8kv_paged_decode_ex",
-               "i8kv_prefix_prefill_int8", "i8kv_prefix_prefill_bf16pv", "i8kv_decode_step_int8"):
+               "i8kv_prefix_prefill_int8", "i8kv_prefix_prefill_bf16pv", "i8kv_decode_step_int8",
+               "i8kv_paged_decode_bf16qk"):
         assert op in names
 
 
@@ -189,6 +190,26 @@ def decode_uint8w(d, S=1, max_len=512, max_blocks=32, part=256, G=32, ws=FAKE,
 def test_decode_uint8w_validation(kw, expect):
     assert decode_uint8w(desc(), **kw) == expect
     assert decode_uint8w(None) == NULL
+
+
+def decode_bf16qk(d, S=1, max_len=512, max_blocks=32, part=256, G=32, ws=FAKE,
+                  ws_bytes=1 << 30, q=FAKE, out=FAKE, scale=0.0625):
+    P = lambda x: None if x is None else C.c_void_p(x)
+    return _lib().i8kv_paged_decode_bf16qk(
+        None if d is None else C.byref(d), S, P(q), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+        P(FAKE), max_blocks, P(FAKE), max_len, part, G, scale, P(ws), ws_bytes, P(out), None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), NULL), (dict(out=None), NULL), (dict(q=FAKE + 2), INVALID),
+    (dict(S=-1), INVALID), (dict(max_len=513, max_blocks=32), INVALID), (dict(G=16), UNSUPPORTED),
+    (dict(part=128), UNSUPPORTED), (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+    (dict(scale=float("inf")), INVALID), (dict(S=0), OK),
+])
+def test_decode_bf16qk_validation(kw, expect):
+    assert decode_bf16qk(desc(), **kw) == expect
+    assert decode_bf16qk(None) == NULL
+    assert decode_bf16qk(desc(D=100)) == UNSUPPORTED
 
 
 def decode_ex(d, opts_kw=None, S=1, max_len=512, max_blocks=32, ws=FAKE, ws_bytes=1 << 30,
