@@ -193,7 +193,7 @@ def time_decode(args, log_prefix=""):
                 decode_us=1e3 * float(np.median(dec_ms)), decode_us_runs=[1e3 * x for x in dec_ms])
 
 
-def time_prefill(reps, G=32, graph=True, bf16pv=False):
+def time_prefill(reps, G=32, graph=True, bf16pv=False, bf16qk=False):
     import numpy as np
     import torch
 
@@ -217,6 +217,10 @@ def time_prefill(reps, G=32, graph=True, bf16pv=False):
     chunk = int(qi.shape[0])
     if bf16pv:  # the BF16-PV ablation of the same call
         run = lambda: K.prefix_prefill_bf16pv(d, q8, qs, qsl, sl, cache, bt, chunk, out=out)
+    elif bf16qk:  # the BF16-QK ablation: the bf16 queries instead of q8 / qs
+        qb = dev(np.ascontiguousarray(wl.query).view(np.int16))
+        run = lambda: K.prefix_prefill_bf16qk(d, qb, qsl, sl, cache, bt, chunk, w_group=G,
+                                              out=out)
     else:
         run = lambda: K.prefix_prefill_int8(d, q8, qs, qsl, sl, cache, bt, chunk, w_group=G,
                                             out=out)
@@ -546,6 +550,9 @@ def main():
             pb = time_prefill(args.prefill_reps, graph=not args.no_graph, bf16pv=True)
             log(f"prefill BF16-PV ablation: {pb['us']:.1f} us")
             extra["prefill_bf16pv_us"] = round(pb["us"], 2)
+            pq = time_prefill(args.prefill_reps, graph=not args.no_graph, bf16qk=True)
+            log(f"prefill BF16-QK ablation: {pq['us']:.1f} us")
+            extra["prefill_bf16qk_us"] = round(pq["us"], 2)
         extra.update(prefill_us=round(pf["us"], 2), prefill_int8_tops=round(pf["tops"], 2),
                      prefill_frac_of_int8_peak=round(pf["tops"] / INT8_PEAK_TOPS, 4),
                      prefill_ops=pf["ops"])

@@ -1,7 +1,7 @@
 /*
  * i8kv -- paged attention over an INT8 KV cache, native to AMD MI355X (gfx950).
  *
- * C ABI of the library libi8kv.so.  Ten calls, on the operations defined on the pages
+ * C ABI of the library libi8kv.so.  Eleven calls, on the operations defined on the pages
  *   [KV] "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
  *        DCU" (part 1 of the series), and
  *   [PV] "Implementing INT8 PV MMAC on a gfx936 DCU: V-scale fusion,
@@ -25,6 +25,7 @@
  *   i8kv_prefix_prefill_bf16pv -- the prefill with a bf16 PV product ([PV] 5)
  *   i8kv_paged_decode_bf16qk -- the decode with a bf16 QK product (the
  *                              pages' QK comparison, [KV] 4.1)
+ *   i8kv_prefix_prefill_bf16qk -- the prefill with a bf16 QK product ([KV] 4.1)
  *
  * Conventions for every call
  *  - Tensor arguments are DEVICE pointers owned by the caller, C-contiguous in
@@ -357,6 +358,28 @@ i8kv_status i8kv_prefix_prefill_bf16pv(const i8kv_cache_desc* desc, int32_t num_
                                        const float* k_scale, const float* v_scale,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        float softmax_scale, void* workspace,
+                                       size_t workspace_bytes, float* out,
+                                       i8kv_stream_t stream);
+
+/*
+ * The BF16-QK ablation of i8kv_prefix_prefill_int8 ([KV] 4.1): the queries
+ * are not quantized; each landed K tile is converted to bf16 (exact for int8
+ * codes) and S = Q K^T runs on v_mfma_f32_16x16x32_bf16 with fp32
+ * accumulation, score = (dot * sK) * softmax_scale.  The online softmax, the
+ * int8 W groups and the PV product are those of i8kv_prefix_prefill_int8
+ * (workgroups of 128 flattened rows instead of 192).
+ *   query_bf16 [total_q, Hq, D] bf16 bits (16-byte aligned) in place of
+ *   q_int8 and q_scale; every other argument and the errors as
+ *   i8kv_prefix_prefill_int8.
+ */
+i8kv_status i8kv_prefix_prefill_bf16qk(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                       int32_t total_q, int32_t max_query_len,
+                                       const uint16_t* query_bf16,
+                                       const int32_t* query_start_loc, const int32_t* seq_lens,
+                                       const int8_t* k_cache, const int8_t* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       int32_t w_group, float softmax_scale, void* workspace,
                                        size_t workspace_bytes, float* out,
                                        i8kv_stream_t stream);
 

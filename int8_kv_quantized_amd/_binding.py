@@ -102,6 +102,9 @@ def load_library():
     lib.i8kv_prefix_prefill_workspace_bytes.argtypes = [D, I32, I32]
     lib.i8kv_prefix_prefill_bf16pv.restype = C.c_int
     lib.i8kv_prefix_prefill_bf16pv.argtypes = ([D, I32, I32, I32] + [P] * 9 + [I32, F, P, SZ, P, P])
+    lib.i8kv_prefix_prefill_bf16qk.restype = C.c_int
+    lib.i8kv_prefix_prefill_bf16qk.argtypes = ([D, I32, I32, I32] + [P] * 8 + [I32, I32, F, P,
+                                                                              SZ, P, P])
     lib.i8kv_prefix_prefill_int8.restype = C.c_int
     lib.i8kv_prefix_prefill_int8.argtypes = ([D, I32, I32, I32] + [P] * 9 + [I32, I32, F, P, SZ,
                                                                             P, P])
@@ -539,3 +542,37 @@ def prefix_prefill_bf16pv(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq
     return prefix_prefill_int8(desc, q_int8, q_scale, query_start_loc, seq_lens, cache,
                                block_tables, max_query_len, softmax_scale=softmax_scale,
                                out=out, workspace=workspace, stream=stream, _bf16pv=True)
+
+
+def prefix_prefill_bf16qk(desc: CacheDesc, query, query_start_loc, seq_lens, cache: PagedCache,
+                          block_tables, max_query_len: int, w_group: int = 32,
+                          softmax_scale: Optional[float] = None, out=None, workspace=None,
+                          stream=None):
+    """The BF16-QK ablation of prefix_prefill_int8: ``query`` [total_q, Hq, D]
+    bf16 (torch.bfloat16, or its bits as int16 / uint16), not quantized;
+    the other arguments as prefix_prefill_int8."""
+    import torch
+    lib = load_library()
+    Tq = int(query.shape[0])
+    S = int(seq_lens.shape[0])
+    Hq, D = desc.num_q_heads, desc.head_dim
+    _check(query, "query", (torch.bfloat16, torch.int16, torch.uint16), (Tq, Hq, D))
+    _check(query_start_loc, "query_start_loc", torch.int32, (S + 1,))
+    _check(seq_lens, "seq_lens", torch.int32, (S,))
+    cache.check(desc)
+    _check(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError(f"block_tables: shape {tuple(block_tables.shape)}, expected ({S}, *)")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((Tq, Hq, D), dtype=torch.float32, device=query.device)
+    _check(out, "out", torch.float32, (Tq, Hq, D))
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.i8kv_prefix_prefill_bf16qk(
+        C.byref(desc), S, Tq, int(max_query_len), _ptr(query), _ptr(query_start_loc),
+        _ptr(seq_lens), _ptr(cache.k_cache), _ptr(cache.v_cache), _ptr(cache.k_scale),
+        _ptr(cache.v_scale), _ptr(block_tables), int(block_tables.shape[1]), int(w_group),
+        float(softmax_scale), _ptr(workspace), int(ws_bytes), _ptr(out), _stream(stream))
+    _raise("prefix_prefill_bf16qk", st)
+    return out

@@ -93,13 +93,14 @@ i8kv_status run_prefill(const i8kv_cache_desc* desc, int32_t num_seqs,
                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                                      int32_t w_group, float softmax_scale, void* workspace,
                                      size_t workspace_bytes, float* out,
-                                     i8kv_stream_t stream, bool pv_bf16) {
+                                     i8kv_stream_t stream, bool pv_bf16,
+                                     const uint16_t* q_bf16 = nullptr) {
   (void)workspace;
   (void)workspace_bytes;
   i8kv_status st = check_desc(desc);
   if (st != I8KV_OK) return st;
-  if (!q_int8 || !q_scale || !query_start_loc || !seq_lens || !k_cache || !v_cache ||
-      !k_scale || !v_scale || !block_tables || !out)
+  if ((!q_bf16 && (!q_int8 || !q_scale)) || !query_start_loc || !seq_lens || !k_cache ||
+      !v_cache || !k_scale || !v_scale || !block_tables || !out)
     return I8KV_ERR_NULL;
   if (num_seqs < 0 || total_q < 0 || max_query_len < 0 || max_blocks_per_seq <= 0)
     return I8KV_ERR_INVALID_ARG;
@@ -107,7 +108,8 @@ i8kv_status run_prefill(const i8kv_cache_desc* desc, int32_t num_seqs,
   if (!std::isfinite(softmax_scale)) return I8KV_ERR_INVALID_ARG;
   if (w_group != 32 && w_group != 64) return I8KV_ERR_UNSUPPORTED;
   if (num_seqs > kMaxGridYZ) return I8KV_ERR_UNSUPPORTED;
-  if (!aligned16(q_int8) || !aligned16(k_cache) || !aligned16(v_cache))
+  if ((q_bf16 ? !aligned16(q_bf16) : !aligned16(q_int8)) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
     return I8KV_ERR_INVALID_ARG;
   if (num_seqs == 0 || total_q == 0) return I8KV_OK;
   PrefillArgs a{};
@@ -123,8 +125,9 @@ i8kv_status run_prefill(const i8kv_cache_desc* desc, int32_t num_seqs,
   a.w_group = w_group;
   a.pv_bf16 = pv_bf16 ? 1 : 0;
   a.softmax_scale = softmax_scale;
-  a.q_int8 = q_int8;
-  a.q_scale = q_scale;
+  a.q_int8 = q_bf16 ? nullptr : q_int8;
+  a.q_scale = q_bf16 ? nullptr : q_scale;
+  a.q_bf16 = q_bf16;
   a.query_start_loc = query_start_loc;
   a.seq_lens = seq_lens;
   a.k_cache = k_cache;
@@ -428,6 +431,23 @@ i8kv_status i8kv_prefix_prefill_bf16pv(const i8kv_cache_desc* desc, int32_t num_
                      seq_lens, k_cache, v_cache, k_scale, v_scale, block_tables,
                      max_blocks_per_seq, 64, softmax_scale, workspace, workspace_bytes, out,
                      stream, true);
+}
+
+i8kv_status i8kv_prefix_prefill_bf16qk(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                       int32_t total_q, int32_t max_query_len,
+                                       const uint16_t* query_bf16,
+                                       const int32_t* query_start_loc, const int32_t* seq_lens,
+                                       const int8_t* k_cache, const int8_t* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       int32_t w_group, float softmax_scale, void* workspace,
+                                       size_t workspace_bytes, float* out,
+                                       i8kv_stream_t stream) {
+  if (!query_bf16) return I8KV_ERR_NULL;
+  return run_prefill(desc, num_seqs, total_q, max_query_len, nullptr, nullptr, query_start_loc,
+                     seq_lens, k_cache, v_cache, k_scale, v_scale, block_tables,
+                     max_blocks_per_seq, w_group, softmax_scale, workspace, workspace_bytes, out,
+                     stream, false, query_bf16);
 }
 
 }  // extern "C"

@@ -47,8 +47,6 @@ namespace i8kv {
 
 namespace {
 
-constexpr int kNW = 12;            // waves per workgroup
-constexpr int kRows = 16 * kNW;    // flattened rows per workgroup
 constexpr int kKT = 64;            // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;      // rescale threshold (log2 units)
@@ -86,6 +84,26 @@ __device__ __forceinline__ int k_lds_off(int key) {  // offset of chunk 0 of `ke
   return (key >> 4) * (D * 16 + 128) + 16 * kperm(key & 15);
 }
 
+// Waves per workgroup (16 flattened rows each): 12; 8 for the BF16-QK
+// ablation, whose bf16 queries take twice the registers.
+template <bool QB>
+struct PrefillShape {
+  static constexpr int NW = QB ? 8 : 12;
+  static constexpr int Rows = 16 * NW;
+};
+
+// BF16-QK: the K tile converted to bf16, one row of D values per key plus 8
+// values of padding; within each 32-key group the keys of QK chain b sit at
+// rows 16b .. 16b + 15 in the order of the MFMA's A rows, so the 16 lanes of
+// one operand read consecutive rows (no bank conflict).
+template <int D>
+struct PrefillKb {
+  static constexpr int Pitch = D + 8;  // bf16 elements per row
+  __device__ static int row(int key) {  // key = 32g + 8q + 4b + i -> 32g + 16b + 4q + i
+    return (key & ~31) + 16 * ((key >> 2) & 1) + 4 * ((key >> 3) & 3) + (key & 3);
+  }
+};
+
 template <int D>
 struct PrefillTile {
   static constexpr int kBytes = kKT / 16 * (D * 16 + 128);  // K tile (pages 128 B apart)
@@ -99,11 +117,19 @@ struct PrefillTile {
 // straight into O; the output is rescaled at every growth of the running max
 // (as the per-tile reference of the online softmax), since bf16 rounding,
 // unlike the group quantization, depends on the reference.
-template <int D, int G, bool BPV>
-__global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs a) {
+// QB: the BF16-QK ablation -- the bf16 queries (not quantized) against the
+// int8 K codes taken exactly as bf16: each K tile, once landed, is converted
+// to bf16 in LDS by the whole workgroup, and S^T = K Q^T runs on
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation; score = dot * sK * scale.
+template <int D, int G, bool BPV, bool QB>
+__global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_kernel(
+    PrefillArgs a) {
+  constexpr int kNW = PrefillShape<QB>::NW;
+  constexpr int kRows = PrefillShape<QB>::Rows;
   constexpr int NC = D / 64;   // 64-dim k-steps of QK
   constexpr int NN = D / 16;   // 16-dim output tiles of PV
   constexpr int NT = kNW * kWave;
+  constexpr int KBP = PrefillKb<D>::Pitch;
   constexpr int KB = PrefillTile<D>::kBytes, VB = PrefillTile<D>::vBytes;
   constexpr int NPC = PrefillTile<D>::kPieces, PPP = PrefillTile<D>::kPagePieces;
   constexpr int kMaxBt = 4096;                    // block-table entries kept in LDS
@@ -113,6 +139,7 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
   __shared__ __attribute__((aligned(16))) float s_sk[2][kKT];
   __shared__ __attribute__((aligned(16))) float s_sv[2][kKT];
   __shared__ int s_bt[kMaxBt];
+  __shared__ __attribute__((aligned(16))) uint16_t s_kb[QB ? kKT * KBP : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lg = lane >> 4, lr = lane & 15;
@@ -135,15 +162,28 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
   const int pos = ctx + tok;
   const size_t qrow = (size_t)(q0 + tok) * a.num_q_heads + (size_t)kv * grp + head;
 
-  v4i qb[NC];
+  v4i qb[QB ? 1 : NC];
+  v4u qh[QB ? NC : 1][2];  // QB: bf16 dims 64c + 16lg + 8e .. +7 of this lane's row
+  if constexpr (QB) {
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-    qb[c] = row_ok ? *reinterpret_cast<const v4i*>(a.q_int8 + qrow * D + 64 * c + 16 * lg)
-                   : v4i{0, 0, 0, 0};
-  // score in log2 units: s2 = acc * sK * (sQ * softmax_scale * log2 e).  A row
-  // past the chunk gets crow = 1 and mref = +inf, which makes all its p~ zero
-  // without a select (its queries are zero, so its scores are 0 or -inf).
-  const float crow = row_ok ? a.q_scale[qrow] * a.softmax_scale * kLog2e : 1.0f;
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        qh[c][e] = row_ok ? *reinterpret_cast<const v4u*>(a.q_bf16 + qrow * D + 64 * c +
+                                                          16 * lg + 8 * e)
+                          : v4u{0u, 0u, 0u, 0u};
+  } else {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qb[c] = row_ok ? *reinterpret_cast<const v4i*>(a.q_int8 + qrow * D + 64 * c + 16 * lg)
+                     : v4i{0, 0, 0, 0};
+  }
+  // score in log2 units: s2 = acc * sK * (sQ * softmax_scale * log2 e) (QB:
+  // s2 = dot * sK * (softmax_scale * log2 e)).  A row past the chunk gets
+  // crow = 1 and mref = +inf, which makes all its p~ zero without a select
+  // (its queries are zero, so its scores are 0 or -inf).
+  const float crow =
+      row_ok ? (QB ? 1.0f : a.q_scale[qrow]) * a.softmax_scale * kLog2e : 1.0f;
 
   const int last_fr = min(row0 + kRows, nrows_seq) - 1;
   const int nkeys = ctx + last_fr / grp + 1;  // keys visible to the workgroup's last row
@@ -217,6 +257,17 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
   // every copy of this wave has landed in LDS (the barrier that follows makes
   // all waves' copies visible)
   auto wait_tile = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // QB: K tile `buf` (landed and visible) -> bf16 rows of s_kb; unit u is the
+  // 16 head-dim bytes of chunk u / 64 of key u % 64.  A barrier must follow.
+  auto convert_k = [&](int buf) {
+    for (int u = tid; u < kKT * (D / 16); u += NT) {
+      const int key = u & (kKT - 1), ch = u / kKT;
+      const v4u kw = *reinterpret_cast<const v4u*>(s_k[buf] + k_lds_off<D>(key) + 256 * ch);
+      uint16_t* dst = s_kb + PrefillKb<D>::row(key) * KBP + 16 * ch;
+      *reinterpret_cast<v8bf*>(dst) = i8x8_to_bf16(kw[0], kw[1]);
+      *reinterpret_cast<v8bf*>(dst + 8) = i8x8_to_bf16(kw[2], kw[3]);
+    }
+  };
 
   float mref = row_ok ? -INFINITY : INFINITY;  // reference max (log2 units)
   float lsum = 0.0f;                           // this lane's share of l
@@ -237,15 +288,30 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       v4i acc[2];
+      v4f accf[QB ? 2 : 1];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        acc[b] = v4i{0, 0, 0, 0};
-        const int krow = 32 * g + 8 * (lr >> 2) + 4 * b + (lr & 3);  // key of A row lr
-        const int8_t* kp = kt + k_lds_off<D>(krow) + 256 * lg;
+        if constexpr (QB) {
+          // A row lr = key 32g + 8(lr/4) + 4b + lr%4, stored at row 32g + 16b + lr
+          const uint16_t* kp = s_kb + (32 * g + 16 * b + lr) * KBP + 16 * lg;
+          accf[b] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const v4i ka = *reinterpret_cast<const v4i*>(kp + 1024 * c);
-          acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qb[c], acc[b], 0, 0, 0);
+          for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const v8bf ka = *reinterpret_cast<const v8bf*>(kp + 64 * c + 8 * e);
+              accf[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  ka, __builtin_bit_cast(v8bf, qh[c][e]), accf[b], 0, 0, 0);
+            }
+        } else {
+          acc[b] = v4i{0, 0, 0, 0};
+          const int krow = 32 * g + 8 * (lr >> 2) + 4 * b + (lr & 3);  // key of A row lr
+          const int8_t* kp = kt + k_lds_off<D>(krow) + 256 * lg;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const v4i ka = *reinterpret_cast<const v4i*>(kp + 1024 * c);
+            acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ka, qb[c], acc[b], 0, 0, 0);
+          }
         }
       }
       const float4 sk0 = *reinterpret_cast<const float4*>(&s_sk[buf][32 * g + 8 * lg]);
@@ -253,7 +319,7 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
       const float skv[8] = {sk0.x, sk0.y, sk0.z, sk0.w, sk1.x, sk1.y, sk1.z, sk1.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float x = (float)acc[j >> 2][j & 3] * skv[j];
+        float x = (QB ? accf[j >> 2][j & 3] : (float)acc[j >> 2][j & 3]) * skv[j];
         if constexpr (MASK) x = (k0 + 32 * g + 8 * lg + j <= pos) ? x : -INFINITY;
         u2[g][j] = x;
         mt = fmaxf(mt, x);
@@ -374,6 +440,10 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const int k0 = t * kKT;
+    if constexpr (QB) {
+      convert_k(buf);
+      __syncthreads();
+    }
     if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);  // in flight during this tile's compute
     if (k0 < wave_nkeys) {
       if (k0 + kKT - 1 > wave_min_pos) compute_tile(buf, k0, std::true_type{});
@@ -397,16 +467,23 @@ __global__ __launch_bounds__(kNW * kWave) void prefix_prefill_kernel(PrefillArgs
 hipError_t launch_prefix_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0 || a.max_query_len == 0) return hipSuccess;
   const int64_t rows = (int64_t)a.max_query_len * a.group;
-  const int64_t tiles = (rows + kRows - 1) / kRows;
+  const bool qb = a.q_bf16 != nullptr;
+  const int64_t per_wg = qb ? PrefillShape<true>::Rows : PrefillShape<false>::Rows;
+  const int64_t tiles = (rows + per_wg - 1) / per_wg;
   dim3 grid((unsigned)tiles, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-  dim3 block(kNW * kWave);
-#define I8KV_PREFILL_CASE(DD, GG)                                                       \
-  if (a.head_dim == DD && (a.pv_bf16 ? GG == 64 : a.w_group == GG)) {                   \
-    if (a.pv_bf16)                                                                      \
-      hipLaunchKernelGGL((prefix_prefill_kernel<DD, GG, true>), grid, block, 0, stream, a); \
-    else                                                                                \
-      hipLaunchKernelGGL((prefix_prefill_kernel<DD, GG, false>), grid, block, 0, stream, a); \
-    return hipGetLastError();                                                           \
+  dim3 block((qb ? PrefillShape<true>::NW : PrefillShape<false>::NW) * kWave);
+#define I8KV_PREFILL_CASE(DD, GG)                                                              \
+  if (a.head_dim == DD && (a.pv_bf16 ? GG == 64 : a.w_group == GG)) {                          \
+    if (qb)                                                                                    \
+      hipLaunchKernelGGL((prefix_prefill_kernel<DD, GG, false, true>), grid, block, 0, stream, \
+                         a);                                                                   \
+    else if (a.pv_bf16)                                                                        \
+      hipLaunchKernelGGL((prefix_prefill_kernel<DD, GG, true, false>), grid, block, 0, stream, \
+                         a);                                                                   \
+    else                                                                                       \
+      hipLaunchKernelGGL((prefix_prefill_kernel<DD, GG, false, false>), grid, block, 0,        \
+                         stream, a);                                                           \
+    return hipGetLastError();                                                                  \
   }
   I8KV_PREFILL_CASE(64, 32)
   I8KV_PREFILL_CASE(64, 64)
