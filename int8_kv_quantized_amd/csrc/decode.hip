@@ -191,6 +191,38 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
   // otherwise sink them past the wait for the sequence length)
   asm volatile("" ::: "memory");
 
+  // ---- second round trip: the scales and K bytes of the partition (V follows
+  // once this wave's QK has consumed K, so V reuses its registers and K is not
+  // queued behind V).  Entries past the sequence are clamped to a valid page:
+  // what they load is discarded (scores of tokens >= L are -inf and their W
+  // and scales are 0), so no load is conditional.  The fused step issues these
+  // loads before its quantization, which then runs while they are in flight.
+  auto clamp_page = [&](int pg) { return min(max(pg, 0), a.num_blocks - 1); };
+  float sk[PPW];
+  float sv_ld;
+  v4i kb[PPW][NC];
+  auto second_round_trip = [&]() {
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) pidk[j] = clamp_page(pidk[j]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) pidv[g] = clamp_page(pidv[g]);
+    pids = clamp_page(pids);
+#pragma unroll
+    for (int j = 0; j < PPW; ++j)
+      sk[j] = a.k_scale[((size_t)pidk[j] * kBlockSize + lr) * Hkv + kv];
+    sv_ld = a.v_scale[((size_t)pids * kBlockSize + (tsv & 15)) * Hkv + kv];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      const int8_t* base = a.k_cache + ((size_t)pidk[j] * Hkv + kv) * (size_t)(D / 16) * 256;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kb[j][c] = *reinterpret_cast<const v4i*>(base + (4 * c + lg) * 256 + lr * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (FUSED) second_round_trip();
+
   const int L = min(max(L_raw, 0), a.max_seq_len);
   const int P_s = (L + kPartition - 1) / kPartition;
   // a row's output element: fp32, or bf16 (nearest, ties to even)
@@ -257,32 +289,7 @@ __global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_parti
     vis[r] = MQ ? L - nq + h / grp + 1 : L;
     obase[r] = qrow(h) * D;
   }
-  // Entries past the sequence are clamped to a valid page: what they load is
-  // discarded (scores of tokens >= L are -inf and their W and scales are 0).
-  auto clamp_page = [&](int pg) { return min(max(pg, 0), a.num_blocks - 1); };
-#pragma unroll
-  for (int j = 0; j < PPW; ++j) pidk[j] = clamp_page(pidk[j]);
-#pragma unroll
-  for (int g = 0; g < 4; ++g) pidv[g] = clamp_page(pidv[g]);
-  pids = clamp_page(pids);
-
-  // ---- second round trip: the scales and K bytes of the partition, then (once
-  // this wave's QK has consumed K, so V reuses its registers and K is not
-  // queued behind V) the V bytes; no load is conditional, each wait partial --
-  float sk[PPW];
-#pragma unroll
-  for (int j = 0; j < PPW; ++j) sk[j] = a.k_scale[((size_t)pidk[j] * kBlockSize + lr) * Hkv + kv];
-  const float sv_ld = a.v_scale[((size_t)pids * kBlockSize + (tsv & 15)) * Hkv + kv];
-  __builtin_amdgcn_sched_barrier(0);
-  v4i kb[PPW][NC];
-#pragma unroll
-  for (int j = 0; j < PPW; ++j) {
-    const int8_t* base = a.k_cache + ((size_t)pidk[j] * Hkv + kv) * (size_t)(D / 16) * 256;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      kb[j][c] = *reinterpret_cast<const v4i*>(base + (4 * c + lg) * 256 + lr * 16);
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!FUSED) second_round_trip();
 #pragma unroll
   for (int j = 0; j < PPW; ++j)
     if (tok0 + 16 * (w * PPW + j) + lr >= L) sk[j] = 0.0f;
