@@ -28,7 +28,7 @@ def test_header_declares_the_operations():
     for op in ("i8kv_kv_quantize_write", "i8kv_kv_quantize_write_rope", "i8kv_paged_decode_int8",
                "i8kv_paged_decode_bf16pv", "i8kv_paged_decode_uint8w", "i8kv_paged_decode_ex",
                "i8kv_prefix_prefill_int8", "i8kv_prefix_prefill_bf16pv", "i8kv_decode_step_int8",
-               "i8kv_paged_decode_bf16qk"):
+               "i8kv_paged_decode_bf16qk", "i8kv_prefix_prefill_bf16qk"):
         assert op in names
 
 
@@ -286,6 +286,25 @@ def test_decode_step_descriptor_checked_first():
 ])
 def test_prefill_validation(kw, expect):
     assert prefill(desc(), **kw) == expect
+
+
+def prefill_bf16qk(d, S=1, Tq=8, max_q=8, G=32, q=FAKE, qsl=FAKE, scale=0.0625):
+    P = lambda x: None if x is None else C.c_void_p(x)
+    return _lib().i8kv_prefix_prefill_bf16qk(
+        None if d is None else C.byref(d), S, Tq, max_q, P(q), P(qsl), P(FAKE), P(FAKE),
+        P(FAKE), P(FAKE), P(FAKE), P(FAKE), 32, G, scale, None, 0, P(FAKE), None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(S=-1), INVALID), (dict(Tq=-1), INVALID), (dict(max_q=9), INVALID),
+    (dict(G=16), UNSUPPORTED), (dict(scale=float("nan")), INVALID),
+    (dict(q=None), NULL), (dict(qsl=None), NULL), (dict(q=FAKE + 2), INVALID),
+    (dict(S=0), OK), (dict(Tq=0, max_q=0), OK),
+])
+def test_prefill_bf16qk_validation(kw, expect):
+    assert prefill_bf16qk(desc(), **kw) == expect
+    assert prefill_bf16qk(None) == NULL
+    assert prefill_bf16qk(desc(D=100)) == UNSUPPORTED
 
 
 def test_binding_rejects_missing_library(monkeypatch, tmp_path):
