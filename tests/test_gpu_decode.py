@@ -120,3 +120,11 @@ def test_decode_cfg3_batch16(orc):
 @pytest.mark.parametrize("G", [32, 64])
 def test_decode_cfg5_mha(orc, G):
     run_decode(W.cfg5_mha_producer_decode(G), orc, G)
+
+
+def test_decode_long_sequences_many_merge_rounds(orc):
+    """150001 and 70000 tokens: 586 and 274 partitions, so the merge runs
+    ten and five rounds of 64 partitions, with ragged last partitions."""
+    wl = W.make_workload("long_decode", seq_lens=(150001, 70000), new_tokens=(1, 1),
+                         num_q_heads=4, num_kv_heads=1, head_dim=64, seed=69)
+    run_decode(wl, orc, 32, report=False)

@@ -84,3 +84,12 @@ def test_prefill_zero_vectors(orc, G):
     wl.key[::11, 1, :] = 0           # some keys of KV head 1
     wl.value[3::13, 0, :] = 0        # some values of KV head 0
     run_prefill(wl, orc, G)
+
+
+def test_prefill_history_beyond_lds_block_table(orc):
+    """70000 history tokens = 4378 pages, more than the 4096 block-table
+    entries the kernel caches in LDS: every page id is then read from the
+    block table in global memory.  Sampled rows of a 40-token chunk."""
+    wl = W.make_workload("history_70k", seed=68, kind="prefill", seq_lens=(70040,),
+                         new_tokens=(40,), num_q_heads=2, num_kv_heads=1, head_dim=64)
+    run_prefill(wl, orc, 32, rows=[0, 1, 17, 38, 39])
