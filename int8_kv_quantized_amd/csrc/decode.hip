@@ -15,7 +15,7 @@
 //
 // Two kernels, no cross-workgroup synchronization:
 //
-// 1. paged_decode_partition_kernel: one workgroup of 8 waves (4 for D = 64)
+// 1. paged_decode_partition_kernel: one workgroup of 8 waves (4 for D <= 128)
 //    per (256-token partition, KV head, sequence).  Two load round trips:
 //    (1) sequence length, block-table entries, queries and their scales;
 //    (2) all scales and K bytes of the partition (16-byte loads), then each
@@ -24,7 +24,7 @@
 //    * QK: v_mfma_i32_16x16x64_i8, A = the GQA group's int8 queries (rows =
 //      q heads, zero-padded to 16), B = one page: lane l holds the 16
 //      head-dim bytes of token l%16 in chunk 4c + l/16.  Wave w owns pages
-//      2w, 2w+1 (4w..4w+3 for D = 64).  Scores of the real heads go to LDS.
+//      2w, 2w+1 (4w..4w+3 for D <= 128).  Scores of the real heads go to LDS.
 //    * Softmax and W quantization: wave h owns head h, lane l tokens
 //      4l..4l+3, so max and sum are one-wave reductions and no lane works on
 //      padding rows.  The chain is the definition's fp32 one (fp32 exp rounded
@@ -35,7 +35,7 @@
 //      bytes); the MFMA over 64 tokens consumes pages 4g..4g+3, lane group j
 //      page 4g+j.  G = 64: one MFMA per group; G = 32: operand A is masked to
 //      lane groups {0,1} resp. {2,3} so each MFMA consumes exactly one group.
-//      Wave w owns output dims [w D/8, (w+1) D/8).
+//      Wave w owns output dims [w D/NW, (w+1) D/NW) of the NW waves.
 //    A single-partition sequence writes the output; otherwise (m_p, l_p, o_p)
 //    go to the workspace.
 // 2. paged_decode_merge_kernel: one wave per (q head, sequence, 64 output
@@ -72,7 +72,7 @@ DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t grou
 // Waves per partition workgroup and the work of each.
 template <int D>
 struct DecodeShape {
-  static constexpr int NW = D >= 128 ? 8 : 4;  // waves
+  static constexpr int NW = D >= 256 ? 8 : 4;  // waves (4 for D <= 128: more workgroups per CU)
   static constexpr int PPW = 16 / NW;          // pages per wave in QK
   static constexpr int DW = D / NW;            // output dims per wave in PV
   static constexpr int NCW = DW / 16;          // 16-dim PV tiles per wave
