@@ -82,11 +82,21 @@ struct DecodeShape {
 // bf16), and UINT8 W groups (codes 0..255 against max W / 255).
 enum : int { kPvInt8 = 0, kPvBf16 = 1, kPvUint8 = 2 };
 
+// Minimum waves per SIMD the compiler must allow: 4 for the int8-PV D = 128
+// kernels (they fit 128 VGPRs without spilling, so four 4-wave workgroups share
+// a CU: the many-workgroup MHA decode measured 126 -> 122 us); the others keep
+// what their registers give (the UINT8-W and ablation variants would spill).
+template <int D, int PVM, bool QB>
+constexpr int decode_min_waves() {
+  return (D == 128 && PVM == kPvInt8 && !QB) ? 4 : 1;
+}
+
 // QB: the BF16-QK ablation -- the bf16 queries (not quantized) against the
 // int8 K codes taken exactly as bf16, v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation, score = (dot * sK) * softmax_scale; the rest is unchanged.
 template <int D, int G, bool FUSED, int PVM, bool MQ, bool QB>
-__global__ __launch_bounds__(DecodeShape<D>::NW * kWave) void paged_decode_partition_kernel(
+__global__ __launch_bounds__(DecodeShape<D>::NW * kWave, (decode_min_waves<D, PVM, QB>())) void
+paged_decode_partition_kernel(
     DecodeArgs a) {
   constexpr bool BPV = PVM == kPvBf16;
   constexpr bool U8W = PVM == kPvUint8;
