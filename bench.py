@@ -496,9 +496,16 @@ def cpu_baseline(wl, G, seconds):
         if el >= seconds:
             break
     gbs = wl.effective_kv_bytes() * reps / el / 1e9
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(line.split(":", 1)[1].strip() for line in f
+                         if line.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return dict(value=round(gbs, 4), unit="GB/s", cores=1, kind="oracle",
                 sample=f"{reps} whole decode calls of {wl.name} ({el:.1f} s, single thread; "
-                       f"host has {os.cpu_count()} logical CPUs)")
+                       f"host has {os.cpu_count()} logical CPUs, {model})")
 
 
 def copy_calibration(mb, reps=10):
