@@ -34,6 +34,10 @@
 //    operand A is V^T, 8 tokens of one dim from the LDS copy of the page.  The
 //    output O^T keeps lane l on row l%16, so sW, alpha and l are per-lane
 //    scalars and the group rescale O += sW * float(C) needs no exchange.
+//    For G = 32 the MFMA accumulator starts at a bias that makes its int32
+//    result readable as fp32 without a conversion, and the two groups of a
+//    tile are folded into O with three VALU operations per element instead
+//    of four (see the PV step).
 //  * Online softmax in base 2 (log2 e folded into the per-row constant);
 //    the output is rescaled only when the running max grows by more than 8
 //    (p~ stays below 2^8), which is exact in real arithmetic since Wq and O
@@ -50,6 +54,8 @@ namespace {
 constexpr int kKT = 64;            // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;      // rescale threshold (log2 units)
+constexpr float kMagic = 12582912.0f;      // 1.5 * 2^23
+constexpr int kMagicBits = 0x4B400000;     // its fp32 bit pattern
 
 // Reduce over the four lanes that share a row (lanes r, r+16, r+32, r+48).
 __device__ __forceinline__ float row_max4(float v) {
@@ -271,6 +277,8 @@ __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_k
 
   float mref = row_ok ? -INFINITY : INFINITY;  // reference max (log2 units)
   float lsum = 0.0f;                           // this lane's share of l
+  float rc = 0.0f;                             // G = 32: offset carried by O (per row)
+  const v4i mag4 = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
   float O[NN][4];
 #pragma unroll
   for (int n = 0; n < NN; ++n)
@@ -333,6 +341,7 @@ __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_k
                                : 1.0f;
       if (grow) mref = mt;
       lsum *= alpha;
+      rc *= alpha;
 #pragma unroll
       for (int n = 0; n < NN; ++n)
 #pragma unroll
@@ -405,17 +414,37 @@ __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_k
     const int8_t* vt = s_v[buf];
     const int voff = 8 * (lg & 1);
     if constexpr (G == 32) {
+      // Both groups of the tile in one pass, the int32 -> fp32 conversion done
+      // by the MFMA: its accumulator starts at the bit pattern of kMagic, so
+      // the result read as fp32 is exactly kMagic + acc (|acc| <= 32 * 127^2 <
+      // 2^22 keeps it inside the binade [2^23, 2^24), where one unit of the
+      // bit pattern is 1.0).  With sW cut to 22 significant bits (a relative
+      // change below 2^-21) the products P_g = kMagic * sW_g are exact, and
+      //   fma(sW1, x1, fma(sW0, x0, -S)) = sW0 acc0 + sW1 acc1 + d,
+      // S = fl(P0 + P1), d = P0 + P1 - S exactly (Fast2Sum, P_g >= 0); d is
+      // per row and is taken off once at the end (rc).  The one rounding left
+      // per element is that of the inner fma, whose value is about -P1:
+      // at most ~sW1 / 2^1, i.e. under one unit of a single Wq * Vq product.
+      const float sw0 = bits_f(f_bits(swg[0]) & ~3u), sw1 = bits_f(f_bits(swg[1]) & ~3u);
+      const float p0 = kMagic * sw0, p1 = kMagic * sw1;
+      const float ph = fmaxf(p0, p1), pl = fminf(p0, p1);
+      const float S = ph + pl;
+      rc += pl - (S - ph);
+      const float nS = -S;
+      const long wb0 = (long)(((uint64_t)wpk[0][1] << 32) | wpk[0][0]);
+      const long wb1 = (long)(((uint64_t)wpk[1][1] << 32) | wpk[1][0]);
+      const int8_t* vp0 = vt + ((lg >> 1) * D + lr) * 16 + voff;
+      const int8_t* vp1 = vt + ((2 + (lg >> 1)) * D + lr) * 16 + voff;
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const long wb = (long)(((uint64_t)wpk[g][1] << 32) | wpk[g][0]);
-        const int8_t* vp = vt + ((2 * g + (lg >> 1)) * D + lr) * 16 + voff;
+      for (int n = 0; n < NN; ++n) {
+        const long va0 = *reinterpret_cast<const long*>(vp0 + 256 * n);
+        const long va1 = *reinterpret_cast<const long*>(vp1 + 256 * n);
+        const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(va0, wb0, mag4, 0, 0, 0);
+        const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(va1, wb1, mag4, 0, 0, 0);
 #pragma unroll
-        for (int n = 0; n < NN; ++n) {
-          const long va = *reinterpret_cast<const long*>(vp + 256 * n);
-          const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(va, wb, v4i{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) O[n][i] += swg[g] * (float)c[i];
-        }
+        for (int i = 0; i < 4; ++i)
+          O[n][i] += __builtin_fmaf(sw1, bits_f((uint32_t)c1[i]),
+                                    __builtin_fmaf(sw0, bits_f((uint32_t)c0[i]), nS));
       }
     } else {
       const long wb0 = (long)(((uint64_t)wpk[0][1] << 32) | wpk[0][0]);
@@ -461,7 +490,8 @@ __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_k
 #pragma unroll
   for (int n = 0; n < NN; ++n)
     *reinterpret_cast<float4*>(dst + 16 * n) =
-        make_float4(O[n][0] * inv, O[n][1] * inv, O[n][2] * inv, O[n][3] * inv);
+        make_float4((O[n][0] - rc) * inv, (O[n][1] - rc) * inv, (O[n][2] - rc) * inv,
+                    (O[n][3] - rc) * inv);
 }
 
 hipError_t launch_prefix_prefill(const PrefillArgs& a, hipStream_t stream) {
