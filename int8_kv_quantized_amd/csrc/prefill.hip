@@ -65,6 +65,20 @@ __device__ __forceinline__ float row_max4(float v) {
   swap32(f_bits(v), a, b);
   return fmaxf(bits_f(a), bits_f(b));
 }
+// Maxima of two non-negative values over the four lanes of a row: integer
+// max on the bit patterns (non-negative floats order like their bits, so no
+// NaN quieting is needed), one reduce-scatter for both values -- after the
+// first swap each 16-lane row holds one value's pair maximum -- and one more
+// swap that hands every lane both results.
+__device__ __forceinline__ void row_max4_pair_nonneg(float x0, float x1, float& m0, float& m1) {
+  auto r = __builtin_amdgcn_permlane16_swap(f_bits(x0), f_bits(x1), false, false);
+  uint32_t m = max((uint32_t)r[0], (uint32_t)r[1]);
+  r = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+  m = max((uint32_t)r[0], (uint32_t)r[1]);
+  r = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+  m0 = bits_f(r[0]);
+  m1 = bits_f(r[1]);
+}
 __device__ __forceinline__ float row_sum4(float v) {
   uint32_t a, b;
   swap16(f_bits(v), a, b);
@@ -349,7 +363,7 @@ __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_k
     }
     // p~ = 2^(s2 - mref), W = p~ sV, Wq = round(W * 127 / max W)
     uint32_t wpk[2][2];
-    float swg[2], am[2], Wv[2][8];
+    float swg[2], am[2], mxg[2], Wv[2][8];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const float4 sv0 = *reinterpret_cast<const float4*>(&s_sv[buf][32 * g + 8 * lg]);
@@ -371,8 +385,9 @@ __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_k
         lsum += pt;
         mx = fmaxf(mx, Wv[g][j]);
       }
-      am[g] = row_max4(mx);
+      mxg[g] = mx;
     }
+    row_max4_pair_nonneg(mxg[0], mxg[1], am[0], am[1]);
     if constexpr (BPV) {
       // ---- O^T += V^T W^T in bf16 (keys of group g: the lane's 8 W values)
       const int8_t* vt = s_v[buf];
