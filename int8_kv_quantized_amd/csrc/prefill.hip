@@ -462,16 +462,21 @@ __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_k
                                     __builtin_fmaf(sw0, bits_f((uint32_t)c0[i]), nS));
       }
     } else {
-      const long wb0 = (long)(((uint64_t)wpk[0][1] << 32) | wpk[0][0]);
-      const long wb1 = (long)(((uint64_t)wpk[1][1] << 32) | wpk[1][0]);
+      // G = 64: the whole tile is one group, consumed by one K = 64 MFMA per
+      // 16-dim tile (gfx950's full-rate int8 shape; two chained K = 32 ones
+      // take twice the matrix-core cycles).  The lane's 16 bytes of operand B
+      // are its 8 keys of each half (8(l/16) .. +7 and 32 + 8(l/16) .. +7), and
+      // operand A carries V of the same 16 keys in the same byte positions, so
+      // the product sums exactly the tile's 64 keys.
+      const v4i wb = {(int)wpk[0][0], (int)wpk[0][1], (int)wpk[1][0], (int)wpk[1][1]};
       const int8_t* vp0 = vt + ((lg >> 1) * D + lr) * 16 + voff;
       const int8_t* vp1 = vt + ((2 + (lg >> 1)) * D + lr) * 16 + voff;
 #pragma unroll
       for (int n = 0; n < NN; ++n) {
-        const long va0 = *reinterpret_cast<const long*>(vp0 + 256 * n);
-        const long va1 = *reinterpret_cast<const long*>(vp1 + 256 * n);
-        v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(va0, wb0, v4i{0, 0, 0, 0}, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_i32_16x16x32_i8(va1, wb1, c, 0, 0, 0);
+        const uint2 va0 = *reinterpret_cast<const uint2*>(vp0 + 256 * n);
+        const uint2 va1 = *reinterpret_cast<const uint2*>(vp1 + 256 * n);
+        const v4i va = {(int)va0.x, (int)va0.y, (int)va1.x, (int)va1.y};
+        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(va, wb, v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[n][i] += swg[0] * (float)c[i];
       }
