@@ -56,6 +56,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;      // rescale threshold (log2 units)
 constexpr float kMagic = 12582912.0f;      // 1.5 * 2^23
 constexpr int kMagicBits = 0x4B400000;     // its fp32 bit pattern
+constexpr int kPvAhead = 2;               // PV: V operands read this many 16-dim tiles ahead
 
 // Reduce over the four lanes that share a row (lanes r, r+16, r+32, r+48).
 __device__ __forceinline__ float row_max4(float v) {
@@ -450,10 +451,23 @@ __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_k
       const long wb1 = (long)(((uint64_t)wpk[1][1] << 32) | wpk[1][0]);
       const int8_t* vp0 = vt + ((lg >> 1) * D + lr) * 16 + voff;
       const int8_t* vp1 = vt + ((2 + (lg >> 1)) * D + lr) * 16 + voff;
+      // V operands read kPvAhead 16-dim tiles ahead of their MFMAs, so the
+      // LDS latency is not on each MFMA's path (2 measured 3% faster than the
+      // compiler's own order; 4 and 6 less)
+      constexpr int PD = kPvAhead;
+      long ra0[PD], ra1[PD];
+#pragma unroll
+      for (int q = 0; q < PD; ++q) {
+        ra0[q] = *reinterpret_cast<const long*>(vp0 + 256 * q);
+        ra1[q] = *reinterpret_cast<const long*>(vp1 + 256 * q);
+      }
 #pragma unroll
       for (int n = 0; n < NN; ++n) {
-        const long va0 = *reinterpret_cast<const long*>(vp0 + 256 * n);
-        const long va1 = *reinterpret_cast<const long*>(vp1 + 256 * n);
+        const long va0 = ra0[n % PD], va1 = ra1[n % PD];
+        if (n + PD < NN) {
+          ra0[n % PD] = *reinterpret_cast<const long*>(vp0 + 256 * (n + PD));
+          ra1[n % PD] = *reinterpret_cast<const long*>(vp1 + 256 * (n + PD));
+        }
         const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(va0, wb0, mag4, 0, 0, 0);
         const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(va1, wb1, mag4, 0, 0, 0);
 #pragma unroll
@@ -471,10 +485,20 @@ __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_k
       const v4i wb = {(int)wpk[0][0], (int)wpk[0][1], (int)wpk[1][0], (int)wpk[1][1]};
       const int8_t* vp0 = vt + ((lg >> 1) * D + lr) * 16 + voff;
       const int8_t* vp1 = vt + ((2 + (lg >> 1)) * D + lr) * 16 + voff;
+      constexpr int PD = kPvAhead;
+      uint2 ra0[PD], ra1[PD];
+#pragma unroll
+      for (int q = 0; q < PD; ++q) {
+        ra0[q] = *reinterpret_cast<const uint2*>(vp0 + 256 * q);
+        ra1[q] = *reinterpret_cast<const uint2*>(vp1 + 256 * q);
+      }
 #pragma unroll
       for (int n = 0; n < NN; ++n) {
-        const uint2 va0 = *reinterpret_cast<const uint2*>(vp0 + 256 * n);
-        const uint2 va1 = *reinterpret_cast<const uint2*>(vp1 + 256 * n);
+        const uint2 va0 = ra0[n % PD], va1 = ra1[n % PD];
+        if (n + PD < NN) {
+          ra0[n % PD] = *reinterpret_cast<const uint2*>(vp0 + 256 * (n + PD));
+          ra1[n % PD] = *reinterpret_cast<const uint2*>(vp1 + 256 * (n + PD));
+        }
         const v4i va = {(int)va0.x, (int)va0.y, (int)va1.x, (int)va1.y};
         const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(va, wb, v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
