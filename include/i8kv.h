@@ -327,6 +327,10 @@ size_t i8kv_prefix_prefill_workspace_bytes(const i8kv_cache_desc* desc, int32_t 
  *   block_tables [S, max_blocks_per_seq] int32
  *   max_query_len >= every chunk length (sizes the launch grid)
  *   out [total_q, Hq, D] fp32, fully overwritten.
+ * Numerics: fp32; the codes use a hardware reciprocal of max W (a code may
+ * differ by one on a near-tie of W / sW) and, for w_group 32, the dequantizing
+ * sW is cut to 22 significant bits (relative change < 2^-21), so outputs
+ * follow the definition to rounding, not bit for bit.
  * Errors: NULL, INVALID_ARG, UNSUPPORTED (as for decode), WORKSPACE.
  */
 i8kv_status i8kv_prefix_prefill_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
