@@ -193,7 +193,13 @@ def time_decode(args, log_prefix=""):
                 decode_us=1e3 * float(np.median(dec_ms)), decode_us_runs=[1e3 * x for x in dec_ms])
 
 
-def time_prefill(reps, G=32, graph=True, bf16pv=False, bf16qk=False):
+def time_prefill(reps, G=32, graph=True, bf16pv=False, bf16qk=False, min_rotation_mb=512.0):
+    """The 2048-over-16384 prefill chunk; successive calls read distinct copies
+    of the K/V cache (>= min_rotation_mb in all, as many as there are calls per
+    timed batch) so the 256 MB last-level cache does not hold the K/V of the
+    previous calls (10 calls x 38 MB between reuses at the defaults)."""
+    import math
+
     import numpy as np
     import torch
 
@@ -211,30 +217,35 @@ def time_prefill(reps, G=32, graph=True, bf16pv=False, bf16qk=False):
                         cache)
     q8, qs = K.kv_quantize_write(d, dev(wl.key[qi]), dev(wl.value[qi]),
                                  dev(wl.slot_mapping[qi]), cache, query=dev(wl.query))
+    copies = max(1, math.ceil(min_rotation_mb * 1e6 / cache_bytes(d)))
+    caches = [cache] + [K.PagedCache(cache.k_cache.clone(), cache.v_cache.clone(),
+                                     cache.k_scale.clone(), cache.v_scale.clone())
+                        for _ in range(copies - 1)]
     qsl, sl, bt = dev(wl.query_start_loc), dev(wl.seq_lens), dev(wl.block_tables)
     out = torch.empty((q8.shape[0], d.num_q_heads, d.head_dim), dtype=torch.float32,
                       device="cuda")
     chunk = int(qi.shape[0])
     if bf16pv:  # the BF16-PV ablation of the same call
-        run = lambda: K.prefix_prefill_bf16pv(d, q8, qs, qsl, sl, cache, bt, chunk, out=out)
+        run = lambda i: K.prefix_prefill_bf16pv(d, q8, qs, qsl, sl, caches[i % copies], bt, chunk,
+                                                out=out)
     elif bf16qk:  # the BF16-QK ablation: the bf16 queries instead of q8 / qs
         qb = dev(np.ascontiguousarray(wl.query).view(np.int16))
-        run = lambda: K.prefix_prefill_bf16qk(d, qb, qsl, sl, cache, bt, chunk, w_group=G,
-                                              out=out)
+        run = lambda i: K.prefix_prefill_bf16qk(d, qb, qsl, sl, caches[i % copies], bt, chunk,
+                                                w_group=G, out=out)
     else:
-        run = lambda: K.prefix_prefill_int8(d, q8, qs, qsl, sl, cache, bt, chunk, w_group=G,
-                                            out=out)
-    for _ in range(2):
-        run()
+        run = lambda i: K.prefix_prefill_int8(d, q8, qs, qsl, sl, caches[i % copies], bt, chunk,
+                                              w_group=G, out=out)
+    for i in range(2):
+        run(i)
     torch.cuda.synchronize()
     if graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for _ in range(reps):
-                run()
+            for i in range(reps):
+                run(i)
         replay = g.replay
     else:
-        replay = lambda: [run() for _ in range(reps)]
+        replay = lambda: [run(i) for i in range(reps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -245,7 +256,8 @@ def time_prefill(reps, G=32, graph=True, bf16pv=False, bf16qk=False):
     hist_len = int(wl.seq_lens[0]) - chunk
     visible = sum(hist_len + j + 1 for j in range(chunk))  # causal pairs per head
     ops = 2 * 2 * d.head_dim * d.num_q_heads * visible
-    return dict(us=us, ops=ops, tops=ops / (us * 1e-6) / 1e12, workload=wl.name)
+    return dict(us=us, ops=ops, tops=ops / (us * 1e-6) / 1e12, workload=wl.name,
+                cache_copies_rotated=copies)
 
 
 def time_producer_chunk(tokens, steps=50, min_rotation_mb=512.0):
@@ -550,19 +562,24 @@ def main():
                  step_separate_calls_us=round(r["step_separate_us"], 3),
                  effective_kv_bytes=eff, cache_copies_rotated=r["copies"])
     if not args.no_prefill:
-        pf = time_prefill(args.prefill_reps, graph=not args.no_graph)
+        pf = time_prefill(args.prefill_reps, graph=not args.no_graph,
+                          min_rotation_mb=args.min_rotation_mb)
         log(f"prefill {pf['workload']}: {pf['us']:.1f} us, {pf['tops']:.1f} int8 TOPS "
             f"({100 * pf['tops'] / INT8_PEAK_TOPS:.1f}% of peak)")
         if not args.no_pv_ablation:
-            pb = time_prefill(args.prefill_reps, graph=not args.no_graph, bf16pv=True)
+            pb = time_prefill(args.prefill_reps, graph=not args.no_graph, bf16pv=True,
+                              min_rotation_mb=args.min_rotation_mb)
             log(f"prefill BF16-PV ablation: {pb['us']:.1f} us")
             extra["prefill_bf16pv_us"] = round(pb["us"], 2)
-            pq = time_prefill(args.prefill_reps, graph=not args.no_graph, bf16qk=True)
+            pq = time_prefill(args.prefill_reps, graph=not args.no_graph, bf16qk=True,
+                              min_rotation_mb=args.min_rotation_mb)
             log(f"prefill BF16-QK ablation: {pq['us']:.1f} us")
             extra["prefill_bf16qk_us"] = round(pq["us"], 2)
         extra.update(prefill_us=round(pf["us"], 2), prefill_int8_tops=round(pf["tops"], 2),
                      prefill_frac_of_int8_peak=round(pf["tops"] / INT8_PEAK_TOPS, 4),
-                     prefill_ops=pf["ops"])
+                     prefill_ops=pf["ops"],
+                     prefill_cache_copies_rotated=min(pf["cache_copies_rotated"],
+                                                      args.prefill_reps))
     if not args.no_producer_chunks:
         chunks = {}
         for T in (2242, 4096):
@@ -596,7 +613,8 @@ def main():
                     decode_frac_hbm=round(b / (rr["decode_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
                 log(f"  sweep {name} G={G}: {sweep[f'{name}_G{G}']}")
         for G in ((32, 64) if not args.no_prefill else ()):
-            pf = time_prefill(args.prefill_reps, G, graph=not args.no_graph)
+            pf = time_prefill(args.prefill_reps, G, graph=not args.no_graph,
+                              min_rotation_mb=args.min_rotation_mb)
             sweep[f"prefill_G{G}"] = dict(us=round(pf["us"], 2), tops=round(pf["tops"], 2),
                                           frac_int8=round(pf["tops"] / INT8_PEAK_TOPS, 4))
             log(f"  sweep prefill G={G}: {sweep[f'prefill_G{G}']}")
