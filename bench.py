@@ -185,7 +185,7 @@ def time_decode(args, log_prefix=""):
         replay_ms(g_warm)
     ms_total = replay_ms(g_step)
     sep_ms = replay_ms(g_sep) / args.steps if fused else ms_total / args.steps
-    dec_ms = [replay_ms(g_dec) / args.steps for _ in range(3)]
+    dec_ms = [replay_ms(g_dec) / args.steps for _ in range(5)]  # p50 over 5 batches
     prod_ms = [replay_ms(g_prod) / args.steps for _ in range(3)]
     return dict(wl=wl, desc=d, copies=copies, ms_per_step=ms_total / args.steps, fused=fused,
                 step_separate_us=1e3 * sep_ms,
