@@ -128,3 +128,11 @@ def test_decode_long_sequences_many_merge_rounds(orc):
     wl = W.make_workload("long_decode", seq_lens=(150001, 70000), new_tokens=(1, 1),
                          num_q_heads=4, num_kv_heads=1, head_dim=64, seed=69)
     run_decode(wl, orc, 32, report=False)
+
+
+def test_decode_max_length(orc):
+    """The longest supported sequence, 2^20 tokens (4096 partitions: the merge
+    runs 64 rounds), next to a ragged one 17 tokens shorter."""
+    wl = W.make_workload("max_len_decode", seq_lens=((1 << 20), (1 << 20) - 17), new_tokens=(1, 1),
+                         num_q_heads=2, num_kv_heads=1, head_dim=64, seed=70)
+    run_decode(wl, orc, 32, report=False)
