@@ -44,8 +44,11 @@
  *    from zero; amax = 0 stores scale 0 and all-zero codes.
  *  - Status: argument and shape checks run on the host BEFORE anything is
  *    enqueued; on any non-OK status nothing has been launched, except
- *    I8KV_ERR_LAUNCH, which reports a failed enqueue.  No C++ exception
- *    crosses the ABI.
+ *    I8KV_ERR_LAUNCH, which reports a failed enqueue.  Before enqueuing,
+ *    each call clears the calling thread's pending (non-sticky) HIP error, as
+ *    hipGetLastError() would, so that error describes its own launches; a
+ *    sticky error (an earlier device fault) is still reported.  No C++
+ *    exception crosses the ABI.
  *  - Supported shapes: block_size = 16; head_dim in {64, 128, 256};
  *    Hq % Hkv = 0 with Hq / Hkv <= 16; w_group in {32, 64};
  *    partition_size = 256.  Other values return I8KV_ERR_UNSUPPORTED.

@@ -67,6 +67,11 @@ def load_library():
     if not p.exists():
         raise RuntimeError(f"{p} is missing: build it with int8_kv_quantized_amd.build.build() "
                            "(there is no fallback path)")
+    # torch first: it brings its own HIP runtime into the process, and the
+    # library must bind to that same runtime.  Loaded before torch, the library
+    # pulls in the system one, torch then shares a runtime it was not built
+    # with, and launches fail with hipErrorNoDevice.
+    import torch  # noqa: F401
     lib = C.CDLL(str(p))
     P, I32, F, SZ = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
     D = C.POINTER(CacheDesc)

@@ -33,6 +33,28 @@ i8kv_status check_desc(const i8kv_cache_desc* d) {
 
 i8kv_status from_hip(hipError_t e) { return e == hipSuccess ? I8KV_OK : I8KV_ERR_LAUNCH; }
 
+// The launch wrappers report hipGetLastError() after enqueuing, which also
+// returns an error left behind by any earlier runtime call of the calling
+// thread (not necessarily one of ours).  Each entry point therefore clears that
+// pending, non-sticky error right before it launches, so the status it returns
+// describes its own launches; a sticky error (a device fault) persists and is
+// still reported.
+hipError_t launch_clean(hipError_t (*launch)(const ProducerArgs&, hipStream_t),
+                        const ProducerArgs& a, hipStream_t st) {
+  (void)hipGetLastError();
+  return launch(a, st);
+}
+hipError_t launch_clean(hipError_t (*launch)(const PrefillArgs&, hipStream_t),
+                        const PrefillArgs& a, hipStream_t st) {
+  (void)hipGetLastError();
+  return launch(a, st);
+}
+hipError_t launch_clean(hipError_t (*launch)(const DecodeArgs&, hipStream_t),
+                        const DecodeArgs& a, hipStream_t st) {
+  (void)hipGetLastError();
+  return launch(a, st);
+}
+
 // Shared by the producer entry points; positions == null means no rotation.
 i8kv_status run_producer(const i8kv_cache_desc* desc, int32_t num_tokens, const uint16_t* key,
                          const uint16_t* value, const uint16_t* query, int8_t* q_int8,
@@ -77,7 +99,7 @@ i8kv_status run_producer(const i8kv_cache_desc* desc, int32_t num_tokens, const 
   a.cos_sin = cos_sin;
   a.rotary_dim = rotary_dim;
   a.max_position = max_position;
-  return from_hip(launch_kv_quantize_write(a, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_clean(launch_kv_quantize_write, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -136,7 +158,7 @@ i8kv_status run_prefill(const i8kv_cache_desc* desc, int32_t num_seqs,
   a.v_scale = v_scale;
   a.block_tables = block_tables;
   a.out = out;
-  return from_hip(launch_prefix_prefill(a, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_clean(launch_prefix_prefill, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -270,7 +292,7 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
   a.part_o = reinterpret_cast<float*>(ws + p.off_part_o);
   a.part_ml = reinterpret_cast<float*>(ws + p.off_part_ml);
   a.max_parts = p.max_parts;
-  return from_hip(launch_paged_decode(a, static_cast<hipStream_t>(stream)));
+  return from_hip(launch_clean(launch_paged_decode, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace

@@ -313,3 +313,15 @@ def test_binding_rejects_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "HERE", tmp_path)
     with pytest.raises(RuntimeError, match="no fallback"):
         _binding.load_library()
+
+
+def test_loading_the_library_brings_torch_in_first():
+    """The library must bind to torch's HIP runtime: loading it in a fresh
+    process with nothing else imported also imports torch, before the dlopen."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import int8_kv_quantized_amd as K; "
+            "assert 'torch' not in sys.modules; K.load_library(); "
+            "assert 'torch' in sys.modules; print('ok')" % str(ROOT))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
