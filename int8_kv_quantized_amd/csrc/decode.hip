@@ -222,12 +222,16 @@ paged_decode_partition_kernel(
       sk[j] = a.k_scale[((size_t)pidk[j] * kBlockSize + lr) * Hkv + kv];
     sv_ld = a.v_scale[((size_t)pids * kBlockSize + (tsv & 15)) * Hkv + kv];
     __builtin_amdgcn_sched_barrier(0);
+    // K and V pages are read once per call: non-temporal loads (streaming
+    // hint, no cache retention) -- 16K decode 13.8 -> 12.9 us, 32K 21.0 ->
+    // 19.8 us, batch 16 136 -> 131 us against ordinary loads
 #pragma unroll
     for (int j = 0; j < PPW; ++j) {
       const int8_t* base = a.k_cache + ((size_t)pidk[j] * Hkv + kv) * (size_t)(D / 16) * 256;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        kb[j][c] = *reinterpret_cast<const v4i*>(base + (4 * c + lg) * 256 + lr * 16);
+        kb[j][c] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4i*>(base + (4 * c + lg) * 256 + lr * 16));
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -358,7 +362,8 @@ paged_decode_partition_kernel(
     const int8_t* base = a.v_cache + ((size_t)pidv[g] * Hkv + kv) * (size_t)D * 16;
 #pragma unroll
     for (int c = 0; c < NCW; ++c)
-      vb[g][c] = *reinterpret_cast<const v4i*>(base + (DecodeShape<D>::DW * w + 16 * c + lr) * 16);
+      vb[g][c] = __builtin_nontemporal_load(
+          reinterpret_cast<const v4i*>(base + (DecodeShape<D>::DW * w + 16 * c + lr) * 16));
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
