@@ -387,12 +387,23 @@ __device__ __forceinline__ void rope_wave_vector(float (&x)[D / kWave], int lane
 }
 
 // The lane's D/64 bf16 elements of a D-vector (see quantize_wave_vector).
-template <int D>
+// NT: non-temporal loads (read-once inputs of the producer: the 2242- and
+// 4096-token chunks measured 5-8% faster); the fused decode step reads its one
+// new token with ordinary loads (the streaming hint measured slightly slower).
+template <int D, bool NT = false>
 __device__ __forceinline__ uint2 load_wave_vector(const uint16_t* src, int lane) {
   constexpr int EPL = D / kWave;
-  if constexpr (EPL == 4) return *reinterpret_cast<const uint2*>(src + lane * 4);
-  else if constexpr (EPL == 2) return make_uint2(*reinterpret_cast<const uint32_t*>(src + lane * 2), 0u);
-  else return make_uint2((uint32_t)src[lane], 0u);
+  typedef uint32_t v2u_ __attribute__((ext_vector_type(2)));
+  if constexpr (EPL == 4) {
+    const v2u_* p = reinterpret_cast<const v2u_*>(src + lane * 4);
+    const v2u_ v = NT ? __builtin_nontemporal_load(p) : *p;
+    return make_uint2(v[0], v[1]);
+  } else if constexpr (EPL == 2) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(src + lane * 2);
+    return make_uint2(NT ? __builtin_nontemporal_load(p) : *p, 0u);
+  } else {
+    return make_uint2((uint32_t)(NT ? __builtin_nontemporal_load(src + lane) : src[lane]), 0u);
+  }
 }
 
 // Stores of one quantized token into the paged caches (lane's D/64 codes):

@@ -85,7 +85,7 @@ __device__ __forceinline__ void producer_load(const ProducerArgs& a, const Produ
   if constexpr (ROPE) st.pos = a.positions[tl];
 #pragma unroll
   for (int i = 0; i < TPW; ++i)
-    st.raw[i] = load_wave_vector<D>(it.src + min(i, it.nt - 1) * it.stride, lane);
+    st.raw[i] = load_wave_vector<D, true>(it.src + min(i, it.nt - 1) * it.stride, lane);
 }
 
 // Lane i's cache slot for token i, or -1 for no write: lanes past the item,
