@@ -127,10 +127,14 @@ __device__ __forceinline__ void store_v_page_staged(int8_t* page, int lane,
     *reinterpret_cast<uint4*>(lds + (r + r / 16) * 16) = make_uint4(w[0], w[1], w[2], w[3]);
   }
   asm volatile("" ::: "memory");  // a wave's LDS accesses complete in order
+  // Pages (and Q rows below) are written once and not read back by this
+  // call: non-temporal stores (2242-token chunk 17.6 -> 15.9 us, with RoPE
+  // 21.5 -> 18.3 us, against ordinary stores).
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
     const int r = 64 * i + lane;
-    *reinterpret_cast<uint4*>(page + r * 16) = *reinterpret_cast<const uint4*>(lds + (r + r / 16) * 16);
+    __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(lds + (r + r / 16) * 16),
+                                reinterpret_cast<v4u*>(page + r * 16));
   }
 }
 
@@ -164,7 +168,9 @@ __device__ __forceinline__ void store_q_staged(int8_t* q0, int64_t token_stride,
     const int off = j * 1024 + lane * 16;
     const int t = off / D;
     const uint4 v = *reinterpret_cast<const uint4*>(lds + off);
-    if (t < nt) *reinterpret_cast<uint4*>(q0 + t * token_stride + off % D) = v;
+    if (t < nt)
+      __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w},
+                                  reinterpret_cast<v4u*>(q0 + t * token_stride + off % D));
   }
 }
 
@@ -185,7 +191,7 @@ __device__ __forceinline__ void store_k_page_staged(int8_t* page, int lane,
   for (int j = 0; j < D / 64; ++j) {
     const int r = 64 * j + lane;  // row (chunk r / 16, token r % 16)
     const uint4 v = *reinterpret_cast<const uint4*>(lds + (r / 16) * CS + (r % 16) * 16);
-    *reinterpret_cast<uint4*>(page + r * 16) = v;
+    __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(page + r * 16));
   }
 }
 
