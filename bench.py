@@ -61,8 +61,10 @@ def parse_args():
                    help="skip the producer-alone timing over 2242- and 4096-token chunks")
     p.add_argument("--prefill-reps", type=int, default=10)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--sweep", action="store_true",
-                   help="also time every decode configuration and prefill at G=32/64")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-configuration decode records (every configuration at "
+                        "G=32 and 64)")
+    p.add_argument("--config-steps", type=int, default=50)
     p.add_argument("--separate-step", action="store_true",
                    help="time the step as kv_quantize_write + paged_decode_int8 instead of "
                         "the fused decode_step_int8")
@@ -136,6 +138,10 @@ def time_decode(args, log_prefix=""):
         K.paged_decode_int8(d, dq8, dqs, caches[i % copies], bt, sl, wl.max_seq_len,
                             w_group=args.w_group, workspace=ws, out=out)
 
+    def partials(i):  # the partition kernel alone (stage 1 of the decode call)
+        K.paged_decode_partials(d, dq8, dqs, caches[i % copies], bt, sl, wl.max_seq_len,
+                                w_group=args.w_group, workspace=ws)
+
     def step_separate(i):
         producer(i)
         decode(i)
@@ -180,20 +186,122 @@ def time_decode(args, log_prefix=""):
     g_step = capture(step, args.steps)
     g_sep = capture(step_separate, args.steps) if fused else g_step
     g_dec = capture(decode, args.steps)
+    g_part = capture(partials, args.steps)
     g_prod = capture(producer, args.steps)
     if args.warmup:
         replay_ms(g_warm)
     ms_total = replay_ms(g_step)
     sep_ms = replay_ms(g_sep) / args.steps if fused else ms_total / args.steps
     dec_ms = [replay_ms(g_dec) / args.steps for _ in range(5)]  # p50 over 5 batches
+    part_ms = [replay_ms(g_part) / args.steps for _ in range(5)]
     prod_ms = [replay_ms(g_prod) / args.steps for _ in range(3)]
+    decode(0)
+    torch.cuda.synchronize()
     return dict(wl=wl, desc=d, copies=copies, ms_per_step=ms_total / args.steps, fused=fused,
                 step_separate_us=1e3 * sep_ms,
                 producer_us=1e3 * float(np.median(prod_ms)),
-                decode_us=1e3 * float(np.median(dec_ms)), decode_us_runs=[1e3 * x for x in dec_ms])
+                decode_us=1e3 * float(np.median(dec_ms)), decode_us_runs=[1e3 * x for x in dec_ms],
+                partition_us=1e3 * float(np.median(part_ms)),
+                out=out.cpu().numpy())
 
 
-def time_prefill(reps, G=32, graph=True, bf16pv=False, bf16qk=False, min_rotation_mb=512.0):
+def _graph_us(fn, steps, reps=3):
+    """Median us per call of `steps` calls of fn(i) captured in one HIP graph."""
+    import numpy as np
+    import torch
+    for i in range(2):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    runs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        runs.append(1e3 * e0.elapsed_time(e1) / steps)
+    return float(np.median(runs))
+
+
+def measure_decode_config(wl, groups=(32, 64), steps=50, min_rotation_mb=512.0,
+                          new_tokens_step=False):
+    """One decode configuration at each W group: the decode call, its partition
+    kernel alone (i8kv_paged_decode_partials) and, with ``new_tokens_step``,
+    the producer of every sequence's new tokens (with Q) and producer + decode
+    as one step.  Caches rotated over >= min_rotation_mb of copies.  Returns
+    (record per G, GPU output per G for the accuracy check)."""
+    import numpy as np
+    import torch
+
+    import int8_kv_quantized_amd as K
+    d = K.CacheDesc(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.num_blocks)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    is_q = np.zeros(wl.num_tokens, bool)
+    is_q[wl.query_token_index] = True
+    hist = np.nonzero(~is_q)[0]
+    qi = wl.query_token_index
+    base = K.PagedCache.allocate(d)
+    if hist.size:
+        K.kv_quantize_write(d, dev(wl.key[hist]), dev(wl.value[hist]),
+                            dev(wl.slot_mapping[hist]), base)
+    knew, vnew, snew, qnew = (dev(wl.key[qi]), dev(wl.value[qi]), dev(wl.slot_mapping[qi]),
+                              dev(wl.query))
+    q8, qs = K.kv_quantize_write(d, knew, vnew, snew, base, query=qnew)
+    rows = torch.from_numpy(wl.decode_query_rows()).cuda()
+    dq8, dqs = q8[rows].contiguous(), qs[rows].contiguous()
+    copies = max(1, math.ceil(min_rotation_mb * 1e6 / cache_bytes(d)))
+    caches = [base] + [K.PagedCache(base.k_cache.clone(), base.v_cache.clone(),
+                                    base.k_scale.clone(), base.v_scale.clone())
+                       for _ in range(copies - 1)]
+    bt, sl, L = dev(wl.block_tables), dev(wl.seq_lens), wl.max_seq_len
+    ws = torch.empty(K.paged_decode_workspace_bytes(d, wl.num_seqs, L), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((wl.num_seqs, d.num_q_heads, d.head_dim), dtype=torch.float32,
+                      device="cuda")
+    eff = wl.effective_kv_bytes()
+    recs, outs = {}, {}
+    for G in groups:
+        decode = lambda i: K.paged_decode_int8(d, dq8, dqs, caches[i % copies], bt, sl, L,
+                                               w_group=G, workspace=ws, out=out)
+        part = lambda i: K.paged_decode_partials(d, dq8, dqs, caches[i % copies], bt, sl, L,
+                                                 w_group=G, workspace=ws)
+        us = _graph_us(decode, steps)
+        pus = _graph_us(part, steps)
+        r = dict(decode_us=round(us, 3), decode_gbs=round(eff / (us * 1e-6) / 1e9, 1),
+                 decode_frac_hbm=round(eff / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                 partition_kernel_us=round(pus, 3),
+                 partition_kernel_frac_hbm=round(eff / (pus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+        if new_tokens_step:
+            def producer(i):
+                K.kv_quantize_write(d, knew, vnew, snew, caches[i % copies], query=qnew,
+                                    q_int8=q8, q_scale=qs)
+
+            def step(i):
+                producer(i)
+                dq8.copy_(q8[rows])
+                dqs.copy_(qs[rows])
+                decode(i)
+            r["producer_us"] = round(_graph_us(producer, steps), 3)
+            r["producer_tokens"] = int(qi.shape[0])
+            r["step_us"] = round(_graph_us(step, steps), 3)
+        decode(0)
+        torch.cuda.synchronize()
+        outs[G] = out.cpu().numpy()
+        recs[f"G{G}"] = r
+    del caches, base
+    torch.cuda.empty_cache()
+    return dict(workload=wl.name, effective_kv_bytes=eff, cache_copies_rotated=copies,
+                batch=wl.num_seqs, max_seq_len=L, **recs), outs
+
+
+def time_prefill(reps, G=32, graph=True, bf16pv=False, bf16qk=False, min_rotation_mb=512.0,
+                 keep_rows=None):
     """The 2048-over-16384 prefill chunk; successive calls read distinct copies
     of the K/V cache (>= min_rotation_mb in all, as many as there are calls per
     timed batch) so the 256 MB last-level cache does not hold the K/V of the
@@ -256,8 +364,13 @@ def time_prefill(reps, G=32, graph=True, bf16pv=False, bf16qk=False, min_rotatio
     hist_len = int(wl.seq_lens[0]) - chunk
     visible = sum(hist_len + j + 1 for j in range(chunk))  # causal pairs per head
     ops = 2 * 2 * d.head_dim * d.num_q_heads * visible
+    rows_out = None
+    if keep_rows is not None:  # the output rows kept for the accuracy check
+        run(0)
+        torch.cuda.synchronize()
+        rows_out = out[torch.from_numpy(np.asarray(keep_rows)).cuda()].cpu().numpy()
     return dict(us=us, ops=ops, tops=ops / (us * 1e-6) / 1e12, workload=wl.name,
-                cache_copies_rotated=copies)
+                cache_copies_rotated=copies, rows_out=rows_out)
 
 
 def time_producer_chunk(tokens, steps=50, min_rotation_mb=512.0):
@@ -520,6 +633,141 @@ def cpu_baseline(wl, G, seconds):
                        f"host has {os.cpu_count()} logical CPUs, {model})")
 
 
+def host_threads(cap=16):
+    """CPUs this process may use, at most ``cap`` (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
+
+
+def prefill_sample_rows(chunk=2048, n=256, seed=1004):
+    """The seeded prefill rows of the CPU leg: the first and last row of every
+    32-row tile, plus seeded others up to ``n``."""
+    import numpy as np
+    starts = np.arange(0, chunk, 32)
+    ends = set(starts.tolist()) | set(np.minimum(starts + 31, chunk - 1).tolist())
+    rest = np.array(sorted(set(range(chunk)) - ends))
+    extra = np.random.default_rng(seed).choice(rest, size=max(0, n - len(ends)), replace=False)
+    return np.array(sorted(ends | set(extra.tolist())), np.int32)
+
+
+def fp64_attention_error(gpu, wl, rows=None):
+    """max-abs / mean-abs of GPU outputs against unquantized softmax attention
+    over the bf16 inputs, in fp64 (decode: each sequence's newest query over
+    its tokens; prefill: the given query rows, causal)."""
+    import numpy as np
+
+    import workloads as W
+    Hq, Hkv, D = wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    grp = Hq // Hkv
+    scale = 1.0 / math.sqrt(D)
+    ref = np.zeros(gpu.shape, np.float64)
+    qsl = wl.query_start_loc
+    for b in range(wl.num_seqs):
+        idx = np.nonzero(wl.token_seq == b)[0]
+        idx = idx[np.argsort(wl.token_pos[idx], kind="stable")]
+        Kf = W.bf16_bits_to_f32(wl.key[idx]).astype(np.float64)
+        Vf = W.bf16_bits_to_f32(wl.value[idx]).astype(np.float64)
+        if rows is None:   # decode: row b is the sequence's newest query
+            qrows, pos, dst = [int(qsl[b + 1]) - 1], [Kf.shape[0] - 1], [b]
+        else:
+            sel = [i for i, r in enumerate(rows) if qsl[b] <= r < qsl[b + 1]]
+            ctx = int(wl.seq_lens[b]) - int(qsl[b + 1] - qsl[b])
+            qrows = [int(rows[i]) for i in sel]
+            pos = [ctx + r - int(qsl[b]) for r in qrows]
+            dst = sel
+        if not qrows:
+            continue
+        Q = W.bf16_bits_to_f32(wl.query[qrows]).astype(np.float64)   # [n, Hq, D]
+        pos = np.asarray(pos)
+        mask = np.arange(Kf.shape[0])[None, :] > pos[:, None]
+        for h in range(Hkv):
+            q = Q[:, h * grp:(h + 1) * grp].reshape(-1, D)            # [n*grp, D]
+            sc = (q @ Kf[:, h].T) * scale
+            sc = sc.reshape(len(qrows), grp, -1)
+            sc[np.broadcast_to(mask[:, None, :], sc.shape)] = -np.inf
+            sc -= sc.max(axis=-1, keepdims=True)
+            pr = np.exp(sc)
+            pr /= pr.sum(axis=-1, keepdims=True)
+            o = pr.reshape(-1, Kf.shape[0]) @ Vf[:, h]
+            ref[dst, h * grp:(h + 1) * grp] = o.reshape(len(qrows), grp, D)
+    err = np.abs(gpu.astype(np.float64) - ref)
+    return dict(max_abs=float(err.max()), mean_abs=float(err.mean()))
+
+
+def cpu_leg(args, head, decode_cfgs, prefill_cfg):
+    """The CPU-baseline leg: the oracle timed on bounded samples of the
+    workloads, and its outputs compared with the GPU outputs taken outside the
+    timed regions (max-abs / mean-abs), beside the error of the GPU outputs
+    against unquantized fp64 attention."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    orc = oracle.default()
+    res = {}
+    # the headline baseline: whole 16K decode calls, one thread
+    res["cpu_baseline"] = cpu_baseline(head["wl"], args.w_group, args.cpu_seconds)
+    log(f"cpu baseline: {res['cpu_baseline']}")
+    acc = {}
+
+    def decode_acc(wl, outs):
+        cache, q8, qs = orc.fill(wl)
+        rows = wl.decode_query_rows()
+        rec = {}
+        for G, gpu in outs.items():
+            ref = orc.paged_decode(q8[rows], qs[rows], cache, wl.block_tables, wl.seq_lens,
+                                   num_q_heads=wl.num_q_heads, w_group=G)
+            e = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))
+            rec[f"G{G}"] = dict(vs_oracle_max_abs=float(e.max()),
+                                vs_oracle_mean_abs=float(e.mean()),
+                                vs_fp64_attention=fp64_attention_error(gpu, wl))
+        return rec
+
+    acc[head["wl"].name + "_step"] = decode_acc(head["wl"], {args.w_group: head["out"]})
+    for key, (wl, outs) in decode_cfgs.items():
+        t0 = time.perf_counter()
+        acc[key] = decode_acc(wl, outs)
+        log(f"accuracy {key}: {acc[key]} ({time.perf_counter() - t0:.1f} s)")
+    if prefill_cfg:
+        wl, rows, outs = prefill_cfg["wl"], prefill_cfg["rows"], prefill_cfg["outs"]
+        cache, q8, qs = orc.fill(wl)
+        threads = host_threads()
+        full = np.zeros((wl.query.shape[0], wl.num_q_heads, wl.head_dim), np.float32)
+        rec = {}
+        for G, gpu in outs.items():
+            parts = [rows[i:i + 4] for i in range(0, rows.size, 4)]
+            t0 = time.perf_counter()
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(lambda r: orc.prefix_prefill(q8, qs, wl.query_start_loc, wl.seq_lens,
+                                                         cache, wl.block_tables, w_group=G,
+                                                         rows=r, out=full), parts))
+            el = time.perf_counter() - t0
+            e = np.abs(gpu.astype(np.float64) - full[rows].astype(np.float64))
+            rec[f"G{G}"] = dict(vs_oracle_max_abs=float(e.max()),
+                                vs_oracle_mean_abs=float(e.mean()),
+                                vs_fp64_attention=fp64_attention_error(gpu, wl, rows),
+                                rows=int(rows.size))
+            if G == 32:
+                ctx = int(wl.seq_lens[0]) - int(wl.query.shape[0])
+                ops = 2 * 2 * wl.head_dim * wl.num_q_heads * int(np.sum(ctx + rows + 1))
+                res["cpu_baseline_prefill"] = dict(
+                    value=round(ops / el / 1e12, 6), unit="int8 TOPS", cores=threads,
+                    kind="oracle",
+                    sample=(f"{rows.size} seeded query rows (the first and last row of each "
+                            f"32-row tile and seeded others) of {wl.name}, all {wl.num_q_heads} "
+                            f"heads, G=32, in {el:.1f} s on {threads} host threads, one row "
+                            f"block per thread; whole chunk at this rate: "
+                            f"{el * wl.query.shape[0] / rows.size:.0f} s"))
+                log(f"cpu baseline prefill: {res['cpu_baseline_prefill']}")
+        acc[wl.name.replace("_G32", "")] = rec
+        log(f"accuracy prefill: {rec}")
+    res["accuracy"] = acc
+    return res
+
+
 def copy_calibration(mb, reps=10):
     """A plain device-to-device copy of known size: its FETCH_SIZE/WRITE_SIZE
     counters give the scale factor for the kernels' byte counters."""
@@ -543,9 +791,11 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU component).", file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import int8_kv_quantized_amd as K
+    import workloads as W
     K.load_library()
 
     r = time_decode(args)
@@ -553,19 +803,58 @@ def main():
     eff = wl.effective_kv_bytes()
     step_s = r["ms_per_step"] * 1e-3
     value = eff / step_s / 1e9
-    achieved = eff / (r["decode_us"] * 1e-6) / 1e9
-    log(f"decode: {r['decode_us']:.2f} us/call, producer "
-        f"{r['producer_us']:.2f} us, step {r['ms_per_step'] * 1e3:.2f} us, "
-        f"{achieved:.0f} GB/s effective ({100 * achieved / HBM_PEAK_GBS:.1f}% of peak)")
+    achieved = eff / (r["partition_us"] * 1e-6) / 1e9
+    call_gbs = eff / (r["decode_us"] * 1e-6) / 1e9
+    log(f"decode: call {r['decode_us']:.2f} us ({100 * call_gbs / HBM_PEAK_GBS:.1f}% of peak), "
+        f"partition kernel {r['partition_us']:.2f} us ({100 * achieved / HBM_PEAK_GBS:.1f}%), "
+        f"producer {r['producer_us']:.2f} us, step {r['ms_per_step'] * 1e3:.2f} us")
     extra = dict(decode_us=round(r["decode_us"], 3),
+                 decode_call_frac_hbm=round(call_gbs / HBM_PEAK_GBS, 4),
+                 partition_kernel_us=round(r["partition_us"], 3),
                  producer_us=round(r["producer_us"], 3),
                  step_separate_calls_us=round(r["step_separate_us"], 3),
                  effective_kv_bytes=eff, cache_copies_rotated=r["copies"])
+    decode_cfgs = {}
+    if not args.no_configs:
+        configs = {}
+        for key, build, step in (
+                ("decode_L512", W.cfg1_decode_512, False),
+                ("decode_L4096_outlierV", lambda: W.cfg2_decode(4096), False),
+                ("decode_L8192_outlierV", lambda: W.cfg2_decode(8192), False),
+                ("decode_L16384_outlierV", lambda: W.cfg2_decode(16384), False),
+                ("decode_L32768", W.cfg3_decode_32k, False),
+                ("decode_batch16_L1K-32K", W.cfg3_decode_batch16, False),
+                ("mha_producer_decode_b8", W.cfg5_mha_producer_decode, True)):
+            t0 = time.perf_counter()
+            cwl = build()
+            rec, outs = measure_decode_config(cwl, steps=args.config_steps,
+                                              min_rotation_mb=args.min_rotation_mb,
+                                              new_tokens_step=step)
+            configs[key] = rec
+            decode_cfgs[key] = (cwl, outs)
+            log(f"config {key}: {rec} ({time.perf_counter() - t0:.1f} s)")
+        extra["configs"] = configs
+    prefill_cfg = None
     if not args.no_prefill:
-        pf = time_prefill(args.prefill_reps, graph=not args.no_graph,
-                          min_rotation_mb=args.min_rotation_mb)
-        log(f"prefill {pf['workload']}: {pf['us']:.1f} us, {pf['tops']:.1f} int8 TOPS "
-            f"({100 * pf['tops'] / INT8_PEAK_TOPS:.1f}% of peak)")
+        rows = prefill_sample_rows()
+        pouts, precs = {}, {}
+        for G in (32, 64):
+            pf = time_prefill(args.prefill_reps, G, graph=not args.no_graph,
+                              min_rotation_mb=args.min_rotation_mb, keep_rows=rows)
+            pouts[G] = pf["rows_out"]
+            precs[f"G{G}"] = dict(us=round(pf["us"], 2), int8_tops=round(pf["tops"], 2),
+                                  frac_int8_peak=round(pf["tops"] / INT8_PEAK_TOPS, 4))
+            log(f"prefill {pf['workload']} G={G}: {pf['us']:.1f} us, {pf['tops']:.1f} int8 TOPS "
+                f"({100 * pf['tops'] / INT8_PEAK_TOPS:.1f}% of peak)")
+            if G == 32:
+                extra.update(prefill_us=round(pf["us"], 2),
+                             prefill_int8_tops=round(pf["tops"], 2),
+                             prefill_frac_of_int8_peak=round(pf["tops"] / INT8_PEAK_TOPS, 4),
+                             prefill_ops=pf["ops"],
+                             prefill_cache_copies_rotated=min(pf["cache_copies_rotated"],
+                                                              args.prefill_reps))
+        extra["prefill"] = precs
+        prefill_cfg = dict(wl=W.cfg4_prefill(), rows=rows, outs=pouts)
         if not args.no_pv_ablation:
             pb = time_prefill(args.prefill_reps, graph=not args.no_graph, bf16pv=True,
                               min_rotation_mb=args.min_rotation_mb)
@@ -575,11 +864,6 @@ def main():
                               min_rotation_mb=args.min_rotation_mb)
             log(f"prefill BF16-QK ablation: {pq['us']:.1f} us")
             extra["prefill_bf16qk_us"] = round(pq["us"], 2)
-        extra.update(prefill_us=round(pf["us"], 2), prefill_int8_tops=round(pf["tops"], 2),
-                     prefill_frac_of_int8_peak=round(pf["tops"] / INT8_PEAK_TOPS, 4),
-                     prefill_ops=pf["ops"],
-                     prefill_cache_copies_rotated=min(pf["cache_copies_rotated"],
-                                                      args.prefill_reps))
     if not args.no_producer_chunks:
         chunks = {}
         for T in (2242, 4096):
@@ -596,33 +880,13 @@ def main():
             abl[f"L{L}"] = time_pv_ablation(L)
             log(f"PV ablation L={L}: {abl[f'L{L}']}")
         extra["pv_ablation"] = abl
-    if args.sweep:
-        sweep = {}
-        for name in ["decode_L512", "decode_L4096", "decode_L8192", "decode_L16384",
-                     "decode_L32768", "decode_batch16", "mha_producer_decode"]:
-            for G in (32, 64):
-                a2 = argparse.Namespace(**vars(args))
-                a2.workload, a2.w_group, a2.steps, a2.warmup = name, G, 50, 5
-                rr = time_decode(a2, log_prefix="  sweep ")
-                b = rr["wl"].effective_kv_bytes()
-                sweep[f"{name}_G{G}"] = dict(
-                    decode_us=round(rr["decode_us"], 3), producer_us=round(rr["producer_us"], 3),
-                    step_us=round(rr["ms_per_step"] * 1e3, 3),
-                    step_separate_calls_us=round(rr["step_separate_us"], 3),
-                    decode_gbs=round(b / (rr["decode_us"] * 1e-6) / 1e9, 1),
-                    decode_frac_hbm=round(b / (rr["decode_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
-                log(f"  sweep {name} G={G}: {sweep[f'{name}_G{G}']}")
-        for G in ((32, 64) if not args.no_prefill else ()):
-            pf = time_prefill(args.prefill_reps, G, graph=not args.no_graph,
-                              min_rotation_mb=args.min_rotation_mb)
-            sweep[f"prefill_G{G}"] = dict(us=round(pf["us"], 2), tops=round(pf["tops"], 2),
-                                          frac_int8=round(pf["tops"] / INT8_PEAK_TOPS, 4))
-            log(f"  sweep prefill G={G}: {sweep[f'prefill_G{G}']}")
-        extra["sweep"] = sweep
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.w_group, args.cpu_seconds)
-        log(f"cpu baseline: {cpu}")
+        leg = cpu_leg(args, r, decode_cfgs, prefill_cfg)
+        cpu = leg["cpu_baseline"]
+        if "cpu_baseline_prefill" in leg:
+            extra["cpu_baseline_prefill"] = leg["cpu_baseline_prefill"]
+        extra["accuracy"] = leg["accuracy"]
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -646,7 +910,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": counted_traffic(wl.name, args.w_group),
-                     "kernel": "paged_decode_int8 call (partition + merge kernels)"},
+                     "kernel": ("paged_decode_partition_kernel<256,32> (the decode's partition "
+                                "stage, i8kv_paged_decode_partials), one launch over the whole "
+                                "16K history")},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -141,7 +141,9 @@ i8kv_status i8kv_kv_quantize_write_rope(const i8kv_cache_desc* desc, int32_t num
 /*
  * Bytes of device workspace that i8kv_paged_decode_int8 needs for num_seqs
  * sequences of at most max_seq_len tokens: the per-partition partials
- * (m_p, l_p and the partition output).  Returns 0 for invalid arguments.
+ * (m_p, l_p and the partition output), i.e. the partition-merge space that
+ * [KV] 5.6 requires to be counted in the memory budget next to the int8
+ * pages and their scales.  Returns 0 for invalid arguments.
  */
 size_t i8kv_paged_decode_workspace_bytes(const i8kv_cache_desc* desc, int32_t num_seqs,
                                          int32_t max_seq_len, int32_t partition_size);
@@ -177,6 +179,52 @@ i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs
                                    float softmax_scale, void* workspace,
                                    size_t workspace_bytes, float* out,
                                    i8kv_stream_t stream);
+
+/*
+ * The two stages of i8kv_paged_decode_int8 as separate calls ([PV] 2.2: each
+ * 256-token partition is reduced on its own to (m_p, l_p, o_p), and the
+ * partition outputs are merged with log-sum-exp weights).  Run back to back
+ * over one workspace they give the output of i8kv_paged_decode_int8 bit for
+ * bit.  Apart, they let the partitions of a sequence be computed where its
+ * pages live and merged once (a decode sharded over partitions: a shard that
+ * starts at a multiple of 256 tokens is a sequence of its own whose block
+ * table starts at its first page, since scores, partition softmax and W
+ * groups are relative to the partition).
+ *
+ * i8kv_paged_decode_partials: the arguments of i8kv_paged_decode_int8
+ * without `out`.  Writes, for every sequence s, KV head h, partition
+ * p < ceil(seq_lens[s] / 256) and q head j of the KV head's group of
+ * g = Hq / Hkv (row r = j), into the workspace:
+ *   o  float [S][Hkv][P][g][D] at byte 0:  o_p = sum over the partition's
+ *      W groups of sW * (Wq x Vq), P_i normalized by the partition's l_p;
+ *   ml float [S][Hkv][P][g][2] at byte align256(S * Hkv * P * g * D * 4):
+ *      (m_p, l_p), the partition's max score and sum of exp(score - m_p);
+ * with P = ceil(max_seq_len / 256) (the size that
+ * i8kv_paged_decode_workspace_bytes(desc, S, max_seq_len, 256) covers).
+ * Entries of partitions past a sequence are not written.  Errors as for
+ * i8kv_paged_decode_int8.
+ *
+ * i8kv_paged_decode_merge: reads that workspace (filled by the partials call
+ * for the same desc, S and max_seq_len, or assembled by the caller in the
+ * same layout) and writes out [S, Hq, D] fp32:
+ *   O = sum_p w_p o_p / sum_p w_p,  w_p = l_p exp(m_p - max_p m_p),
+ * over p < ceil(seq_lens[s] / 256); a one-partition sequence gets o_0 itself
+ * and an empty one zeros.  Errors: NULL (desc, seq_lens, workspace, out),
+ * INVALID_ARG / UNSUPPORTED as for i8kv_paged_decode_int8, WORKSPACE.
+ */
+i8kv_status i8kv_paged_decode_partials(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                       const int8_t* q_int8, const float* q_scale,
+                                       const int8_t* k_cache, const int8_t* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, int32_t max_seq_len,
+                                       int32_t partition_size, int32_t w_group,
+                                       float softmax_scale, void* workspace,
+                                       size_t workspace_bytes, i8kv_stream_t stream);
+i8kv_status i8kv_paged_decode_merge(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                    const int32_t* seq_lens, int32_t max_seq_len,
+                                    int32_t partition_size, const void* workspace,
+                                    size_t workspace_bytes, float* out, i8kv_stream_t stream);
 
 /*
  * The BF16-PV ablation of i8kv_paged_decode_int8 ([PV] 5 compares its int8 PV
@@ -252,7 +300,9 @@ typedef struct {
   int32_t out_bf16;        /* 0: out is fp32; 1: out is bf16 bits (nearest, ties to even) */
 } i8kv_decode_opts;
 
-/* Workspace bytes of i8kv_paged_decode_ex (0 for invalid arguments). */
+/* Workspace bytes of i8kv_paged_decode_ex: the partition-merge space of its
+ * nq * (Hq / Hkv) rows per KV head, for the memory budget of [KV] 5.6
+ * (0 for invalid arguments). */
 size_t i8kv_paged_decode_ex_workspace_bytes(const i8kv_cache_desc* desc,
                                             const i8kv_decode_opts* opts, int32_t num_seqs,
                                             int32_t max_seq_len);
@@ -311,7 +361,8 @@ i8kv_status i8kv_decode_step_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
                                   float softmax_scale, void* workspace, size_t workspace_bytes,
                                   float* out, i8kv_stream_t stream);
 
-/* Workspace bytes for i8kv_prefix_prefill_int8 (currently none needed). */
+/* Workspace bytes for i8kv_prefix_prefill_int8, for the memory budget of
+ * [KV] 5.6.  The prefill keeps its (m, l, o) state on chip, so this is 0. */
 size_t i8kv_prefix_prefill_workspace_bytes(const i8kv_cache_desc* desc, int32_t num_seqs,
                                            int32_t total_q);
 

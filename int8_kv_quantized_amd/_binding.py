@@ -6,8 +6,10 @@ contiguity and device) or raw device pointers (ints, trusted as given).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import dataclasses
+import functools
 import math
 from pathlib import Path
 from typing import Optional
@@ -88,6 +90,11 @@ def load_library():
     lib.i8kv_paged_decode_int8.restype = C.c_int
     lib.i8kv_paged_decode_int8.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F, P, SZ,
                                                                  P, P])
+    lib.i8kv_paged_decode_partials.restype = C.c_int
+    lib.i8kv_paged_decode_partials.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F, P,
+                                                                     SZ, P])
+    lib.i8kv_paged_decode_merge.restype = C.c_int
+    lib.i8kv_paged_decode_merge.argtypes = [D, I32, P, I32, I32, P, SZ, P, P]
     lib.i8kv_paged_decode_uint8w.restype = C.c_int
     lib.i8kv_paged_decode_uint8w.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F, P, SZ, P, P])
     O = C.POINTER(DecodeOpts)
@@ -170,6 +177,35 @@ def _stream(stream):
     return C.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(stream):
+    """Context that makes ``stream`` torch's current stream (None: leave it)."""
+    if stream is None:
+        return contextlib.nullcontext()
+    import torch
+    if isinstance(stream, int):
+        if stream == torch.cuda.current_stream().cuda_stream:
+            return contextlib.nullcontext()
+        stream = torch.cuda.ExternalStream(stream)
+    return torch.cuda.stream(stream)
+
+
+def _allocates_on_stream(fn):
+    """Run an entry point with its ``stream`` keyword as torch's current stream.
+
+    Every tensor the binding allocates for the call (workspace, outputs, the
+    quantized queries) is then allocated -- and zero-filled -- on the stream
+    the kernels are enqueued on: the fill is ordered before the launch, and
+    torch's caching allocator hands the block to a later allocation only
+    after the work queued on that stream, never while the kernels may still
+    use it.  ``stream`` must be passed by keyword.
+    """
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        with _on_stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return wrapper
+
+
 def _raise(fn, st):
     if st != I8KV_OK:
         raise I8KVError(fn, st)
@@ -232,6 +268,7 @@ def _producer_args(desc: CacheDesc, key, value, slot_mapping, cache: PagedCache,
     return T, q_int8, q_scale
 
 
+@_allocates_on_stream
 def kv_quantize_write(desc: CacheDesc, key, value, slot_mapping, cache: PagedCache,
                       query=None, q_int8=None, q_scale=None, num_tokens: Optional[int] = None,
                       stream=None):
@@ -251,6 +288,7 @@ def kv_quantize_write(desc: CacheDesc, key, value, slot_mapping, cache: PagedCac
     return q_int8, q_scale
 
 
+@_allocates_on_stream
 def kv_quantize_write_rope(desc: CacheDesc, key, value, slot_mapping, positions, cos_sin,
                            cache: PagedCache, query=None, q_int8=None, q_scale=None,
                            num_tokens: Optional[int] = None, rotary_dim: Optional[int] = None,
@@ -289,7 +327,8 @@ def paged_decode_workspace_bytes(desc: CacheDesc, num_seqs: int, max_seq_len: in
 
 
 def _decode_args(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables, seq_lens,
-                 max_seq_len, partition_size, softmax_scale, workspace, out, q_bf16=None):
+                 max_seq_len, partition_size, softmax_scale, workspace, out, q_bf16=None,
+                 want_out=True):
     import torch
     q_any = q_int8 if q_bf16 is None else q_bf16
     S = int(seq_lens.shape[0]) if _is_tensor(seq_lens) else int(q_any.shape[0])
@@ -310,14 +349,16 @@ def _decode_args(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tabl
         softmax_scale = 1.0 / math.sqrt(D)
     need = paged_decode_workspace_bytes(desc, S, max_seq_len, partition_size)
     if workspace is None:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=block_tables.device)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=block_tables.device)
     ws_bytes = workspace.numel() * workspace.element_size() if _is_tensor(workspace) else need
-    if out is None:
-        out = torch.empty((S, Hq, D), dtype=torch.float32, device=block_tables.device)
-    _check(out, "out", torch.float32, (S, Hq, D))
+    if want_out:
+        if out is None:
+            out = torch.empty((S, Hq, D), dtype=torch.float32, device=block_tables.device)
+        _check(out, "out", torch.float32, (S, Hq, D))
     return S, float(softmax_scale), workspace, int(ws_bytes), out
 
 
+@_allocates_on_stream
 def paged_decode_int8(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables,
                       seq_lens, max_seq_len: int, w_group: int = 32,
                       partition_size: int = 256, softmax_scale: Optional[float] = None,
@@ -325,7 +366,8 @@ def paged_decode_int8(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block
     """Paged decode over the int8 cache; returns ``out`` [S, Hq, D] fp32.
 
     ``workspace`` must hold paged_decode_workspace_bytes(...) bytes and be
-    256-byte aligned (allocated here if None; contents need no initialization).
+    256-byte aligned (allocated here if None); its contents need no
+    initialization.
     """
     lib = load_library()
     S, scale, workspace, ws_bytes, out = _decode_args(
@@ -340,6 +382,52 @@ def paged_decode_int8(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block
     return out
 
 
+@_allocates_on_stream
+def paged_decode_partials(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables,
+                          seq_lens, max_seq_len: int, w_group: int = 32,
+                          partition_size: int = 256, softmax_scale: Optional[float] = None,
+                          workspace=None, stream=None):
+    """Stage 1 of paged_decode_int8 alone: every sequence's per-partition
+    (m_p, l_p, o_p) into ``workspace`` (layout in include/i8kv.h); returns
+    the workspace (allocated here if None)."""
+    lib = load_library()
+    S, scale, workspace, ws_bytes, _ = _decode_args(
+        desc, q_int8, q_scale, cache, block_tables, seq_lens, max_seq_len, partition_size,
+        softmax_scale, workspace, None, want_out=False)
+    st = lib.i8kv_paged_decode_partials(
+        C.byref(desc), S, _ptr(q_int8), _ptr(q_scale), _ptr(cache.k_cache),
+        _ptr(cache.v_cache), _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(partition_size),
+        int(w_group), scale, _ptr(workspace), ws_bytes, _stream(stream))
+    _raise("paged_decode_partials", st)
+    return workspace
+
+
+@_allocates_on_stream
+def paged_decode_merge(desc: CacheDesc, seq_lens, max_seq_len: int, workspace,
+                       partition_size: int = 256, out=None, stream=None):
+    """Stage 2 of paged_decode_int8 alone: merge the partials in ``workspace``
+    into ``out`` [S, Hq, D] fp32 (allocated here if None)."""
+    import torch
+    lib = load_library()
+    _check(seq_lens, "seq_lens", torch.int32)
+    S = int(seq_lens.shape[0])
+    Hq, D = desc.num_q_heads, desc.head_dim
+    if workspace is None:
+        raise ValueError("workspace: the partials to merge are needed")
+    need = paged_decode_workspace_bytes(desc, S, max_seq_len, partition_size)
+    ws_bytes = workspace.numel() * workspace.element_size() if _is_tensor(workspace) else need
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=seq_lens.device)
+    _check(out, "out", torch.float32, (S, Hq, D))
+    st = lib.i8kv_paged_decode_merge(C.byref(desc), S, _ptr(seq_lens), int(max_seq_len),
+                                     int(partition_size), _ptr(workspace), int(ws_bytes),
+                                     _ptr(out), _stream(stream))
+    _raise("paged_decode_merge", st)
+    return out
+
+
+@_allocates_on_stream
 def paged_decode_uint8w(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables,
                         seq_lens, max_seq_len: int, w_group: int = 32,
                         partition_size: int = 256, softmax_scale: Optional[float] = None,
@@ -365,6 +453,7 @@ def paged_decode_ex_workspace_bytes(desc: CacheDesc, opts: DecodeOpts, num_seqs:
         C.byref(desc), C.byref(opts), int(num_seqs), int(max_seq_len)))
 
 
+@_allocates_on_stream
 def paged_decode_ex(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables, seq_lens,
                     max_seq_len: int, queries_per_seq: int = 1, pv: str = "int8",
                     w_group: int = 32, out_bf16: bool = False, partition_size: int = 256,
@@ -393,7 +482,7 @@ def paged_decode_ex(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_t
                       nq, 1 if out_bf16 else 0)
     need = paged_decode_ex_workspace_bytes(desc, opts, S, max_seq_len)
     if workspace is None:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=block_tables.device)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=block_tables.device)
     ws_bytes = workspace.numel() * workspace.element_size() if _is_tensor(workspace) else need
     dt = torch.bfloat16 if out_bf16 else torch.float32
     if out is None:
@@ -408,6 +497,7 @@ def paged_decode_ex(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_t
     return out
 
 
+@_allocates_on_stream
 def paged_decode_bf16pv(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block_tables,
                         seq_lens, max_seq_len: int, partition_size: int = 256,
                         softmax_scale: Optional[float] = None, workspace=None, out=None,
@@ -427,6 +517,7 @@ def paged_decode_bf16pv(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, blo
     return out
 
 
+@_allocates_on_stream
 def paged_decode_bf16qk(desc: CacheDesc, query, cache: PagedCache, block_tables, seq_lens,
                         max_seq_len: int, w_group: int = 32, partition_size: int = 256,
                         softmax_scale: Optional[float] = None, workspace=None, out=None,
@@ -447,6 +538,7 @@ def paged_decode_bf16qk(desc: CacheDesc, query, cache: PagedCache, block_tables,
     return out
 
 
+@_allocates_on_stream
 def decode_step_int8(desc: CacheDesc, key, value, query, cache: PagedCache, block_tables,
                      seq_lens, max_seq_len: int, w_group: int = 32, partition_size: int = 256,
                      softmax_scale: Optional[float] = None, workspace=None, out=None,
@@ -480,7 +572,7 @@ def decode_step_int8(desc: CacheDesc, key, value, query, cache: PagedCache, bloc
         softmax_scale = 1.0 / math.sqrt(D)
     need = paged_decode_workspace_bytes(desc, S, max_seq_len, partition_size)
     if workspace is None:
-        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=block_tables.device)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=block_tables.device)
     ws_bytes = workspace.numel() * workspace.element_size() if _is_tensor(workspace) else need
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.float32, device=block_tables.device)
@@ -500,6 +592,7 @@ def prefix_prefill_workspace_bytes(desc: CacheDesc, num_seqs: int, total_q: int)
         C.byref(desc), int(num_seqs), int(total_q)))
 
 
+@_allocates_on_stream
 def prefix_prefill_int8(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_lens,
                         cache: PagedCache, block_tables, max_query_len: int,
                         w_group: int = 32, softmax_scale: Optional[float] = None,
@@ -538,6 +631,7 @@ def prefix_prefill_int8(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_l
     return out
 
 
+@_allocates_on_stream
 def prefix_prefill_bf16pv(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_lens,
                           cache: PagedCache, block_tables, max_query_len: int,
                           softmax_scale: Optional[float] = None, out=None, workspace=None,
@@ -549,6 +643,7 @@ def prefix_prefill_bf16pv(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq
                                out=out, workspace=workspace, stream=stream, _bf16pv=True)
 
 
+@_allocates_on_stream
 def prefix_prefill_bf16qk(desc: CacheDesc, query, query_start_loc, seq_lens, cache: PagedCache,
                           block_tables, max_query_len: int, w_group: int = 32,
                           softmax_scale: Optional[float] = None, out=None, workspace=None,

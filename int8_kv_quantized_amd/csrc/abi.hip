@@ -229,13 +229,15 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
                        void* workspace, size_t workspace_bytes, float* out,
                        const DecodeArgs* fused, i8kv_stream_t stream, bool pv_bf16 = false,
                        bool w_uint8 = false, int32_t nq = 1, uint16_t* out16 = nullptr,
-                       const uint16_t* q_bf16 = nullptr) {
+                       const uint16_t* q_bf16 = nullptr, int32_t stage = 0) {
   i8kv_status st = check_desc(desc);
   if (st != I8KV_OK) return st;
-  if (!k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !seq_lens ||
-      (!out && !out16))
+  // stage 1 (partitions alone) has no output; stage 2 (merge alone) reads only
+  // the sequence lengths and the workspace
+  if (!seq_lens || (stage != 1 && !out && !out16)) return I8KV_ERR_NULL;
+  if (stage != 2 && (!k_cache || !v_cache || !k_scale || !v_scale || !block_tables))
     return I8KV_ERR_NULL;
-  if (!fused && !q_bf16 && (!q_int8 || !q_scale)) return I8KV_ERR_NULL;
+  if (stage != 2 && !fused && !q_bf16 && (!q_int8 || !q_scale)) return I8KV_ERR_NULL;
   if (fused && (!fused->new_key || !fused->new_value || !fused->new_query)) return I8KV_ERR_NULL;
   if (fused && (!q_int8) != (!q_scale)) return I8KV_ERR_NULL;
   if (num_seqs < 0 || max_seq_len < 0 || max_blocks_per_seq <= 0) return I8KV_ERR_INVALID_ARG;
@@ -249,7 +251,7 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
     return I8KV_ERR_UNSUPPORTED;
   if (max_seq_len > kMaxSeqLen || num_seqs > kMaxGridYZ) return I8KV_ERR_UNSUPPORTED;
   if ((q_int8 && !aligned16(q_int8)) || (q_bf16 && !aligned16(q_bf16)) ||
-      !aligned16(k_cache) || !aligned16(v_cache) ||
+      (k_cache && !aligned16(k_cache)) || (v_cache && !aligned16(v_cache)) ||
       (out && !aligned16(out)) || (out16 && !aligned16(out16)))
     return I8KV_ERR_INVALID_ARG;
   if (fused && (!aligned16(fused->new_key) || !aligned16(fused->new_value) ||
@@ -292,6 +294,7 @@ i8kv_status run_decode(const i8kv_cache_desc* desc, int32_t num_seqs, const int8
   a.part_o = reinterpret_cast<float*>(ws + p.off_part_o);
   a.part_ml = reinterpret_cast<float*>(ws + p.off_part_ml);
   a.max_parts = p.max_parts;
+  a.stage = stage;
   return from_hip(launch_clean(launch_paged_decode, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -312,6 +315,33 @@ i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs
   return run_decode(desc, num_seqs, q_int8, q_scale, k_cache, v_cache, k_scale, v_scale,
                     block_tables, max_blocks_per_seq, seq_lens, max_seq_len, partition_size,
                     w_group, softmax_scale, workspace, workspace_bytes, out, nullptr, stream);
+}
+
+i8kv_status i8kv_paged_decode_partials(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                       const int8_t* q_int8, const float* q_scale,
+                                       const int8_t* k_cache, const int8_t* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* seq_lens, int32_t max_seq_len,
+                                       int32_t partition_size, int32_t w_group,
+                                       float softmax_scale, void* workspace,
+                                       size_t workspace_bytes, i8kv_stream_t stream) {
+  return run_decode(desc, num_seqs, q_int8, q_scale, k_cache, v_cache, k_scale, v_scale,
+                    block_tables, max_blocks_per_seq, seq_lens, max_seq_len, partition_size,
+                    w_group, softmax_scale, workspace, workspace_bytes, nullptr, nullptr, stream,
+                    false, false, 1, nullptr, nullptr, /*stage=*/1);
+}
+
+i8kv_status i8kv_paged_decode_merge(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                    const int32_t* seq_lens, int32_t max_seq_len,
+                                    int32_t partition_size, const void* workspace,
+                                    size_t workspace_bytes, float* out, i8kv_stream_t stream) {
+  // the merge reads no page: a table width that admits max_seq_len, no cache
+  const int32_t width = max_seq_len > 0 ? (max_seq_len + kBlockSize - 1) / kBlockSize : 1;
+  return run_decode(desc, num_seqs, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                    nullptr, width, seq_lens, max_seq_len, partition_size, 32, 1.0f,
+                    const_cast<void*>(workspace), workspace_bytes, out, nullptr, stream, false,
+                    false, 1, nullptr, nullptr, /*stage=*/2);
 }
 
 i8kv_status i8kv_paged_decode_bf16pv(const i8kv_cache_desc* desc, int32_t num_seqs,

@@ -41,6 +41,10 @@
 // 2. paged_decode_merge_kernel: one wave per (q head, sequence, 32 output
 //    dims) merges the partitions, O = sum w_p o_p / sum w_p with
 //    w_p = l_p exp(m_p - M).
+// The two kernels also run alone (DecodeArgs::stage): the partitions with
+// every sequence's partials written to the workspace, or the merge of a
+// workspace so filled -- the split a decode sharded over the partitions of a
+// sequence needs (partials computed where the pages are, merged once).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -83,19 +87,20 @@ struct DecodeShape {
 enum : int { kPvInt8 = 0, kPvBf16 = 1, kPvUint8 = 2 };
 
 // Minimum waves per SIMD the compiler must allow: 4 for the int8-PV D = 128
-// kernels (they fit 128 VGPRs without spilling, so four 4-wave workgroups share
-// a CU: the many-workgroup MHA decode measured 126 -> 122 us); the others keep
-// what their registers give (the UINT8-W and ablation variants would spill).
-template <int D, int PVM, bool QB>
+// kernels that fit 128 VGPRs without spilling, so four 4-wave workgroups share
+// a CU (the many-workgroup MHA decode measured 126 -> 122 us); the others keep
+// what their registers give (the UINT8-W and ablation variants, and the
+// several-query G = 32 variant, would spill under the cap).
+template <int D, int G, int PVM, bool MQ, bool QB>
 constexpr int decode_min_waves() {
-  return (D == 128 && PVM == kPvInt8 && !QB) ? 4 : 1;
+  return (D == 128 && PVM == kPvInt8 && !QB && !(MQ && G == 32)) ? 4 : 1;
 }
 
 // QB: the BF16-QK ablation -- the bf16 queries (not quantized) against the
 // int8 K codes taken exactly as bf16, v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation, score = (dot * sK) * softmax_scale; the rest is unchanged.
 template <int D, int G, bool FUSED, int PVM, bool MQ, bool QB>
-__global__ __launch_bounds__(DecodeShape<D>::NW * kWave, (decode_min_waves<D, PVM, QB>())) void
+__global__ __launch_bounds__(DecodeShape<D>::NW * kWave, (decode_min_waves<D, G, PVM, MQ, QB>())) void
 paged_decode_partition_kernel(
     DecodeArgs a) {
   constexpr bool BPV = PVM == kPvBf16;
@@ -287,11 +292,15 @@ paged_decode_partition_kernel(
     }
   }
   if (L == 0) {
-    if (p == 0)
+    if (p == 0 && a.stage == 0)
       for (int i = tid; i < rows * D; i += NT) put_out(i / D, i % D, 0.0f);
     return;
   }
   if (p >= P_s) return;
+  // one partition and both stages in this call: the partition's output is the
+  // sequence's output (w_0 o_0 / w_0); otherwise the partials go to the
+  // workspace for the merge
+  const bool direct = P_s == 1 && a.stage == 0;
   const int tok0 = p * kPartition;
   // per output row r of this lane (rows 4 lg + r): the causal key limit and
   // the output offset, computed once
@@ -554,7 +563,7 @@ paged_decode_partition_kernel(
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * lg + r;
       if (h < rows) {
-        if (P_s == 1) {
+        if (direct) {
           if (a.out16) a.out16[obase[r] + dim] = (uint16_t)bf16_rne_bits(o[c][r]);
           else a.out[obase[r] + dim] = o[c][r];
         }
@@ -562,7 +571,7 @@ paged_decode_partition_kernel(
       }
     }
   }
-  if (P_s > 1 && tid < rows) {
+  if (!direct && tid < rows) {
     a.part_ml[(node + tid) * 2] = s_M[tid];
     a.part_ml[(node + tid) * 2 + 1] = s_L[tid];
   }
@@ -605,7 +614,25 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
   int L = a.seq_lens[s];
   L = min(max(L, 0), a.max_seq_len);
   const int P_s = (L + kPartition - 1) / kPartition;
-  if (P_s <= 1) return;  // written by the partition kernel
+  const size_t o = (((size_t)s * a.nq + qi) * a.num_q_heads + h) * D + 32 * slice;
+  auto put4 = [&](float x0, float x1, float x2, float x3) {
+    if (a.out16)
+      reinterpret_cast<uint2*>(a.out16 + o)[lane] =
+          make_uint2(bf16_rne_bits(x0) | (bf16_rne_bits(x1) << 16),
+                     bf16_rne_bits(x2) | (bf16_rne_bits(x3) << 16));
+    else
+      reinterpret_cast<float4*>(a.out + o)[lane] = make_float4(x0, x1, x2, x3);
+  };
+  if (a.stage == 0 && P_s <= 1) return;  // written by the partition kernel
+  if (P_s <= 1) {
+    // the merge alone: an empty sequence gives zeros, one partition its own
+    // output (what the partition kernel writes when it runs both stages)
+    if (lane < 8) {
+      if (P_s == 0) put4(0.f, 0.f, 0.f, 0.f);
+      else put4(v[0].x, v[0].y, v[0].z, v[0].w);
+    }
+    return;
+  }
 
   float m = lane < P_s ? ml0.x : -INFINITY;
   for (int q = lane + RP; q < P_s; q += RP) m = fmaxf(m, ml[(size_t)q * rows].x);
@@ -623,11 +650,15 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
     if (q0 > 0) issue(q0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float wq = __shfl(wl, lg + 8 * u, kWave);  // 0 past the sequence
-      acc.x += wq * v[u].x;
-      acc.y += wq * v[u].y;
-      acc.z += wq * v[u].z;
-      acc.w += wq * v[u].w;
+      // Slots of partitions past the sequence were loaded (before L was
+      // known) but never written: whatever they hold, even NaN or Inf, is
+      // dropped by the select, not multiplied by a zero weight.
+      const bool live = q0 + lg + 8 * u < P_s;
+      const float wq = __shfl(wl, lg + 8 * u, kWave);
+      acc.x += live ? wq * v[u].x : 0.0f;
+      acc.y += live ? wq * v[u].y : 0.0f;
+      acc.z += live ? wq * v[u].z : 0.0f;
+      acc.w += live ? wq * v[u].w : 0.0f;
     }
   }
   wsum = group_sumf<kWave>(wsum);
@@ -644,15 +675,7 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
   if (lane < 8) {
     // wsum = 0 only for a query that sees no key at all (seq_len < nq): zeros
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-    const size_t o = (((size_t)s * a.nq + qi) * a.num_q_heads + h) * D + 32 * slice;
-    if (a.out16) {
-      reinterpret_cast<uint2*>(a.out16 + o)[lane] =
-          make_uint2(bf16_rne_bits(r[0] * inv) | (bf16_rne_bits(r[1] * inv) << 16),
-                     bf16_rne_bits(r[2] * inv) | (bf16_rne_bits(r[3] * inv) << 16));
-    } else {
-      reinterpret_cast<float4*>(a.out + o)[lane] =
-          make_float4(r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv);
-    }
+    put4(r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv);
   }
 }
 
@@ -664,6 +687,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.head_dim == DD && (a.pv_bf16 ? GG == 64 : a.w_group == GG)) {                            \
     const dim3 blk(DecodeShape<DD>::NW * kWave);                                                 \
     const bool mq = a.nq > 1;                                                                    \
+    if (a.stage == 2) {                                                                          \
+      hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(kWave), 0, stream, a);     \
+      return hipGetLastError();                                                                  \
+    }                                                                                            \
     if (a.new_key)                                                                               \
       hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8, false, false>),   \
                          grid, blk, 0, stream, a);                                               \
@@ -688,7 +715,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     else                                                                                         \
       hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false, false>),  \
                          grid, blk, 0, stream, a);                                               \
-    if (a.max_parts > 1)                                                                         \
+    if (a.max_parts > 1 && a.stage == 0)                                                         \
       hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(kWave), 0, stream, a);     \
     return hipGetLastError();                                                                    \
   }

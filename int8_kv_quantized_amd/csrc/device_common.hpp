@@ -218,10 +218,6 @@ __device__ __forceinline__ void unpack_wave_vector(uint2 raw, float (&x)[D / kWa
   }
 }
 
-// Returns the lane's codes packed one byte per element and sets `scale`:
-// amax = max |x| over the wave, scale = amax / 127 (IEEE), code =
-// clamp(round(x / scale), -127, 127), and scale 0 with all-zero codes when
-// amax = 0.
 // Codes of a lane's n elements given the vector's scale s (amax / 127) as
 //   sd = s, or 1 when amax = 0 (all elements are then zero), and rs = 1 / sd.
 // Fast rule: qh = fma(x, rs, 128.5 + 2^-14) lies within 1.9e-5 of the IEEE
@@ -252,43 +248,6 @@ __device__ __forceinline__ uint32_t quantize_codes_rs(const float (&x)[n], float
   for (int i = 0; i < n; ++i) packed = __builtin_amdgcn_cvt_pk_u8_f32(floorf(qh[i]), i, packed);
   packed ^= kFlip;
   if (divide || fmin < 0x1p-13f) {
-    packed = 0;
-#pragma unroll
-    for (int i = 0; i < n; ++i) packed |= ((uint32_t)(quantize_code(x[i], sd) & 0xff)) << (8 * i);
-  }
-  return packed;
-}
-
-// Returns the lane's codes packed one byte per element and sets `scale`:
-// amax = max |x| over the wave, scale = amax / 127 (IEEE), code =
-// clamp(round(x / scale), -127, 127), and scale 0 with all-zero codes when
-// amax = 0.
-// Codes of a lane's n elements given the vector's scale s (amax / 127) as
-//   sd = s, or 1 when amax = 0 (all elements are then zero), and rs = 1 / sd.
-// Fast rule: qb = fma(x, rs, 128) lies within 1.9e-5 of the IEEE quotient
-// x / sd plus 128 (|x| <= 127 sd, sd normal), so unless qb is within 2^-13 of
-// a rounding midpoint, rint(qb) - 128 is the code clamp(round(x / sd)) with
-// ties away from zero: it is never a tie and never outside [-127, 127].  The
-// biased code (1..255) is packed by the byte conversion and the bias removed
-// by flipping each byte's top bit.  A lane with an element near a midpoint,
-// or a subnormal sd (1 / sd may overflow), divides instead.  (Checked on the
-// CPU exhaustively for every bf16 x and amax with a normal scale, and on
-// random and near-midpoint fp32 inputs.)
-template <int n>
-__device__ __forceinline__ uint32_t quantize_codes_rs(const float (&x)[n], float sd, float rs) {
-  static_assert(n >= 1 && n <= 4, "at most four codes per lane");
-  constexpr uint32_t kBias = n == 4 ? 0x80808080u : n == 2 ? 0x8080u : 0x80u;
-  bool divide = !(sd >= 0x1p-126f);
-  uint32_t packed = 0;
-#pragma unroll
-  for (int i = 0; i < n; ++i) {
-    const float qb = fmaf(x[i], rs, 128.0f);
-    const float c = rintf(qb);
-    divide |= fabsf(qb - c) > 0.5f - 0x1p-13f;
-    packed = __builtin_amdgcn_cvt_pk_u8_f32(c, i, packed);
-  }
-  packed ^= kBias;
-  if (divide) {
     packed = 0;
 #pragma unroll
     for (int i = 0; i < n; ++i) packed |= ((uint32_t)(quantize_code(x[i], sd) & 0xff)) << (8 * i);

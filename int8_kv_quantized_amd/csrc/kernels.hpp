@@ -74,6 +74,11 @@ struct DecodeArgs {
   float* part_o;    // [S, Hkv, max_parts, group, D]
   float* part_ml;   // [S, Hkv, max_parts, group, 2]
   int32_t max_parts;
+  // The two stages run alone: 1 = partitions only (every sequence's partials
+  // go to the workspace, single-partition ones included, nothing to `out`);
+  // 2 = merge only (every sequence, single-partition and empty ones
+  // included, from the workspace to `out`); 0 = both, as one call.
+  int32_t stage;
 };
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);

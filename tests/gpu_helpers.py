@@ -77,3 +77,33 @@ def report_fp64(got, ref64, what):
     err = np.abs(got.astype(np.float64) - ref64)
     say(f"    {what} vs unquantized fp64 attention: max-abs {err.max():.3e} "
         f"mean-abs {err.mean():.3e}")
+
+
+def host_workers(cap=16):
+    """Threads for oracle work on the host: the CPUs this process may use, at
+    most ``cap`` (the GPU machine gives one GPU's job a 16-CPU share)."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
+
+
+def oracle_rows(fn, rows, out, workers=None, chunk=4):
+    """Fill ``out`` at ``rows`` with ``fn(rows=<int32 array>, out=out)`` run
+    over chunks of rows on a thread pool.  The oracle is a ctypes library, so
+    each call releases the GIL and the chunks run in parallel; each call
+    writes only its own rows of ``out``."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows = np.asarray(rows, np.int32)
+    parts = [rows[i:i + chunk] for i in range(0, rows.size, chunk)]
+    with ThreadPoolExecutor(workers or host_workers()) as ex:
+        list(ex.map(lambda r: fn(rows=r, out=out), parts))
+    return out
+
+
+def row_tile_ends(total_rows, tile=32):
+    """First and last query row of every ``tile``-row tile of a chunk."""
+    starts = np.arange(0, total_rows, tile)
+    return np.unique(np.concatenate([starts, np.minimum(starts + tile - 1, total_rows - 1)]))

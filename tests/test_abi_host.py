@@ -153,6 +153,49 @@ def test_decode_validation(kw, expect):
     assert decode(desc(), **kw) == expect
 
 
+def decode_partials(d, S=1, max_len=512, max_blocks=32, part=256, G=32, ws=FAKE,
+                    ws_bytes=1 << 30, q8=FAKE, bt=FAKE, kc=FAKE, scale=0.0625):
+    P = lambda x: None if x is None else C.c_void_p(x)
+    return _lib().i8kv_paged_decode_partials(
+        None if d is None else C.byref(d), S, P(q8), P(FAKE), P(kc), P(FAKE), P(FAKE), P(FAKE),
+        P(bt), max_blocks, P(FAKE), max_len, part, G, scale, P(ws), ws_bytes, None)
+
+
+def decode_merge(d, S=1, max_len=512, part=256, sl=FAKE, ws=FAKE, ws_bytes=1 << 30, out=FAKE):
+    P = lambda x: None if x is None else C.c_void_p(x)
+    return _lib().i8kv_paged_decode_merge(None if d is None else C.byref(d), S, P(sl), max_len,
+                                         part, P(ws), ws_bytes, P(out), None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q8=None), NULL), (dict(bt=None), NULL), (dict(kc=None), NULL),
+    (dict(kc=FAKE + 4), INVALID), (dict(S=-1), INVALID), (dict(max_len=513), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(part=512), UNSUPPORTED), (dict(G=16), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE), (dict(ws=FAKE + 16), WORKSPACE),
+    (dict(S=0), OK),
+])
+def test_decode_partials_validation(kw, expect):
+    """The partials stage takes no output pointer; everything else as the call."""
+    assert decode_partials(desc(), **kw) == expect
+    assert decode_partials(None) == NULL
+    assert decode_partials(desc(D=100)) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(sl=None), NULL), (dict(out=None), NULL), (dict(out=FAKE + 4), INVALID),
+    (dict(S=-1), INVALID), (dict(max_len=-1), INVALID), (dict(part=128), UNSUPPORTED),
+    (dict(max_len=(1 << 20) + 1), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE), (dict(ws=FAKE + 16), WORKSPACE),
+    (dict(S=0), OK),
+])
+def test_decode_merge_validation(kw, expect):
+    """The merge stage reads only the lengths and the workspace: no query,
+    cache or block table is needed."""
+    assert decode_merge(desc(), **kw) == expect
+    assert decode_merge(None) == NULL
+    assert decode_merge(desc(D=100)) == UNSUPPORTED
+
+
 # --- fused decode step -----------------------------------------------------------
 def decode_bf16pv(d, S=1, max_len=512, max_blocks=32, part=256, ws=FAKE, ws_bytes=1 << 30,
                   q8=FAKE, out=FAKE, scale=0.0625):
@@ -325,3 +368,4 @@ def test_loading_the_library_brings_torch_in_first():
             "assert 'torch' in sys.modules; print('ok')" % str(ROOT))
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
+
