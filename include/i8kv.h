@@ -181,6 +181,35 @@ i8kv_status i8kv_paged_decode_int8(const i8kv_cache_desc* desc, int32_t num_seqs
                                    i8kv_stream_t stream);
 
 /*
+ * i8kv_paged_decode_int8 for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same kernels and
+ * the same output bit for bit.  The per-partition partials go to a fixed
+ * device array inside the library, one per GPU, of
+ * i8kv_paged_decode_noalloc_max_bytes() = 64 MiB, held from the first call on
+ * a GPU until the process ends.  A call whose partials need more
+ * (i8kv_paged_decode_workspace_bytes(desc, S, max_seq_len, 256) > 64 MiB; at
+ * 24 q / 4 KV heads x 256 that is S * max_seq_len above ~690K tokens, e.g.
+ * 16 sequences of up to 32768 fit) returns I8KV_ERR_WORKSPACE before touching
+ * the device.  The call allocates and frees
+ * nothing.  All calls on one GPU share the array: calls that overlap on one
+ * GPU (other streams, other threads) race; serialize them.  The array needs no
+ * initialization.  `stream` must belong to the current device.  Errors as for
+ * i8kv_paged_decode_int8, and LAUNCH if the array's device address cannot be
+ * obtained.
+ */
+size_t i8kv_paged_decode_noalloc_max_bytes(void);
+i8kv_status i8kv_paged_decode_int8_noalloc(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                           const int8_t* q_int8, const float* q_scale,
+                                           const int8_t* k_cache, const int8_t* v_cache,
+                                           const float* k_scale, const float* v_scale,
+                                           const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                           int32_t max_seq_len, int32_t partition_size,
+                                           int32_t w_group, float softmax_scale, float* out,
+                                           i8kv_stream_t stream);
+
+/*
  * The two stages of i8kv_paged_decode_int8 as separate calls ([PV] 2.2: each
  * 256-token partition is reduced on its own to (m_p, l_p, o_p), and the
  * partition outputs are merged with log-sum-exp weights).  Run back to back

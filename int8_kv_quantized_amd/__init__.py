@@ -12,6 +12,7 @@ fails loudly if the library has not been built -- there is no fallback.
     paged_decode_workspace_bytes(desc, num_seqs, max_seq_len)
     paged_decode_int8(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
     paged_decode_partials(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
+    paged_decode_int8_noalloc(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
     paged_decode_merge(desc, seq_lens, max_seq_len, workspace, ...)
     paged_decode_bf16pv(desc, q_int8, q_scale, cache, block_tables, seq_lens, ...)
     paged_decode_bf16qk(desc, query, cache, block_tables, seq_lens, ...)
@@ -41,7 +42,9 @@ from ._binding import (  # noqa: F401
     paged_decode_ex,
     paged_decode_ex_workspace_bytes,
     paged_decode_int8,
+    paged_decode_int8_noalloc,
     paged_decode_merge,
+    paged_decode_noalloc_max_bytes,
     paged_decode_partials,
     paged_decode_uint8w,
     paged_decode_workspace_bytes,

@@ -90,6 +90,11 @@ def load_library():
     lib.i8kv_paged_decode_int8.restype = C.c_int
     lib.i8kv_paged_decode_int8.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F, P, SZ,
                                                                  P, P])
+    lib.i8kv_paged_decode_noalloc_max_bytes.restype = SZ
+    lib.i8kv_paged_decode_noalloc_max_bytes.argtypes = []
+    lib.i8kv_paged_decode_int8_noalloc.restype = C.c_int
+    lib.i8kv_paged_decode_int8_noalloc.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F,
+                                                                         P, P])
     lib.i8kv_paged_decode_partials.restype = C.c_int
     lib.i8kv_paged_decode_partials.argtypes = ([D, I32] + [P] * 7 + [I32, P, I32, I32, I32, F, P,
                                                                      SZ, P])
@@ -379,6 +384,31 @@ def paged_decode_int8(desc: CacheDesc, q_int8, q_scale, cache: PagedCache, block
         int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(partition_size),
         int(w_group), scale, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream))
     _raise("paged_decode_int8", st)
+    return out
+
+
+def paged_decode_noalloc_max_bytes() -> int:
+    return int(load_library().i8kv_paged_decode_noalloc_max_bytes())
+
+
+@_allocates_on_stream
+def paged_decode_int8_noalloc(desc: CacheDesc, q_int8, q_scale, cache: PagedCache,
+                              block_tables, seq_lens, max_seq_len: int, w_group: int = 32,
+                              partition_size: int = 256, softmax_scale: Optional[float] = None,
+                              out=None, stream=None):
+    """paged_decode_int8 without a workspace: the library's fixed per-GPU
+    array holds the partials (see include/i8kv.h for the size limit; calls
+    that overlap on one GPU race).  With ``out`` given, nothing is allocated."""
+    lib = load_library()
+    S, scale, _, _, out = _decode_args(
+        desc, q_int8, q_scale, cache, block_tables, seq_lens, max_seq_len, partition_size,
+        softmax_scale, 0, out)
+    st = lib.i8kv_paged_decode_int8_noalloc(
+        C.byref(desc), S, _ptr(q_int8), _ptr(q_scale), _ptr(cache.k_cache),
+        _ptr(cache.v_cache), _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len), int(partition_size),
+        int(w_group), scale, _ptr(out), _stream(stream))
+    _raise("paged_decode_int8_noalloc", st)
     return out
 
 

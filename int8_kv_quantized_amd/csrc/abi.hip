@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "i8kv.h"
 #include "kernels.hpp"
@@ -443,6 +444,75 @@ i8kv_status i8kv_decode_step_int8(const i8kv_cache_desc* desc, int32_t num_seqs,
   return run_decode(desc, num_seqs, q_int8, q_scale, k_cache, v_cache, k_scale, v_scale,
                     block_tables, max_blocks_per_seq, seq_lens, max_seq_len, partition_size,
                     w_group, softmax_scale, workspace, workspace_bytes, out, &f, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---- the decode for callers that cannot allocate ---------------------------
+// Partials of i8kv_paged_decode_int8_noalloc: a fixed device array, one copy
+// per GPU, alive until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is looked up once
+// per device (with that device current) and only that address is handed to
+// kernels.  Every call on a GPU shares the array; it needs no clearing (the
+// partition kernel writes every partial the merge reads).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on its first use there).
+i8kv_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return I8KV_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return I8KV_ERR_LAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return I8KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t i8kv_paged_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+i8kv_status i8kv_paged_decode_int8_noalloc(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                           const int8_t* q_int8, const float* q_scale,
+                                           const int8_t* k_cache, const int8_t* v_cache,
+                                           const float* k_scale, const float* v_scale,
+                                           const int32_t* block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                           int32_t max_seq_len, int32_t partition_size,
+                                           int32_t w_group, float softmax_scale, float* out,
+                                           i8kv_stream_t stream) {
+  // sizes first: a call that does not fit the fixed array is rejected before
+  // the device is touched
+  const i8kv_status sd = check_desc(desc);
+  if (sd != I8KV_OK) return sd;
+  if (num_seqs > 0 && max_seq_len >= 0 && max_seq_len <= kMaxSeqLen &&
+      partition_size == kPartition) {
+    const DecodePlan p = make_decode_plan(num_seqs, desc->num_kv_heads,
+                                          desc->num_q_heads / desc->num_kv_heads,
+                                          desc->head_dim, max_seq_len);
+    if (p.bytes > kNoAllocScratchBytes) return I8KV_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  const i8kv_status ss = scratch_of_current_device(&ws);
+  if (ss != I8KV_OK) return ss;
+  return run_decode(desc, num_seqs, q_int8, q_scale, k_cache, v_cache, k_scale, v_scale,
+                    block_tables, max_blocks_per_seq, seq_lens, max_seq_len, partition_size,
+                    w_group, softmax_scale, ws, kNoAllocScratchBytes, out, nullptr, stream);
 }
 
 size_t i8kv_prefix_prefill_workspace_bytes(const i8kv_cache_desc* desc, int32_t num_seqs,

@@ -369,3 +369,19 @@ def test_loading_the_library_brings_torch_in_first():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
 
+
+def test_noalloc_decode_size_checks_before_any_device_call():
+    """The no-allocation decode rejects a descriptor or a size past its fixed
+    array before it asks the runtime for anything (no GPU is needed here)."""
+    P = C.c_void_p
+    lib = _lib()
+    assert lib.i8kv_paged_decode_noalloc_max_bytes() == 64 << 20
+    d = desc()
+    args = lambda dd, S, L: (None if dd is None else C.byref(dd), S, P(FAKE), P(FAKE), P(FAKE),
+                             P(FAKE), P(FAKE), P(FAKE), P(FAKE), max(1, L // 16), P(FAKE), L, 256,
+                             32, 0.0625, P(FAKE), None)
+    assert lib.i8kv_paged_decode_int8_noalloc(*args(None, 1, 512)) == NULL
+    assert lib.i8kv_paged_decode_int8_noalloc(*args(desc(D=100), 1, 512)) == UNSUPPORTED
+    assert K.paged_decode_workspace_bytes(d, 32, 32768) > 64 << 20
+    assert lib.i8kv_paged_decode_int8_noalloc(*args(d, 32, 32768)) == WORKSPACE
+    assert K.paged_decode_workspace_bytes(d, 16, 32768) <= 64 << 20
