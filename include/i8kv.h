@@ -429,6 +429,28 @@ i8kv_status i8kv_prefix_prefill_int8(const i8kv_cache_desc* desc, int32_t num_se
                                      i8kv_stream_t stream);
 
 /*
+ * The UINT8-W variant of i8kv_prefix_prefill_int8 ([PV] 6: W = p~ sV >= 0, so
+ * unsigned codes give one more bit): per aligned group of w_group keys
+ *   sW = max W / 255 (IEEE), Wq = round(W / sW) in [0, 255] (half away from
+ *   zero on the definition's division; the kernel's reciprocal rule may move a
+ *   code by one on a near-tie), o = alpha o + sum_g sW (Wq x Vq);
+ * everything else as i8kv_prefix_prefill_int8.  gfx950's int8 MFMA is signed,
+ * so the codes enter it as Wq - 128 and a second MFMA against all-ones rows
+ * returns the group's sum of Vq, of which 128 times is added back in int32
+ * (exact).  Arguments and errors as for i8kv_prefix_prefill_int8.
+ */
+i8kv_status i8kv_prefix_prefill_uint8w(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                       int32_t total_q, int32_t max_query_len,
+                                       const int8_t* q_int8, const float* q_scale,
+                                       const int32_t* query_start_loc, const int32_t* seq_lens,
+                                       const int8_t* k_cache, const int8_t* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       int32_t w_group, float softmax_scale, void* workspace,
+                                       size_t workspace_bytes, float* out,
+                                       i8kv_stream_t stream);
+
+/*
  * The BF16-PV ablation of i8kv_prefix_prefill_int8 ([PV] 5): the same scores
  * and online softmax, but W = p~ * sV is rounded to bf16 (nearest, ties to
  * even) instead of group-quantized, and o = alpha o + sum_i bf16(W_i) Vq_i

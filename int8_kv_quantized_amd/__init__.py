@@ -24,6 +24,7 @@ fails loudly if the library has not been built -- there is no fallback.
     prefix_prefill_bf16pv(desc, q_int8, q_scale, query_start_loc, seq_lens,
                           cache, block_tables, ...)
     prefix_prefill_bf16qk(desc, query, query_start_loc, seq_lens, cache, block_tables, ...)
+    prefix_prefill_uint8w(desc, q_int8, q_scale, query_start_loc, seq_lens, cache, ...)
     decode_step_int8(desc, key, value, query, cache, block_tables, seq_lens, ...)
 """
 from ._binding import (  # noqa: F401
@@ -51,6 +52,7 @@ from ._binding import (  # noqa: F401
     prefix_prefill_bf16pv,
     prefix_prefill_bf16qk,
     prefix_prefill_int8,
+    prefix_prefill_uint8w,
     prefix_prefill_workspace_bytes,
     status_string,
 )

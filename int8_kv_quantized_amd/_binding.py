@@ -122,6 +122,9 @@ def load_library():
     lib.i8kv_prefix_prefill_bf16qk.restype = C.c_int
     lib.i8kv_prefix_prefill_bf16qk.argtypes = ([D, I32, I32, I32] + [P] * 8 + [I32, I32, F, P,
                                                                               SZ, P, P])
+    lib.i8kv_prefix_prefill_uint8w.restype = C.c_int
+    lib.i8kv_prefix_prefill_uint8w.argtypes = ([D, I32, I32, I32] + [P] * 9 + [I32, I32, F, P, SZ,
+                                                                              P, P])
     lib.i8kv_prefix_prefill_int8.restype = C.c_int
     lib.i8kv_prefix_prefill_int8.argtypes = ([D, I32, I32, I32] + [P] * 9 + [I32, I32, F, P, SZ,
                                                                             P, P])
@@ -626,7 +629,7 @@ def prefix_prefill_workspace_bytes(desc: CacheDesc, num_seqs: int, total_q: int)
 def prefix_prefill_int8(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_lens,
                         cache: PagedCache, block_tables, max_query_len: int,
                         w_group: int = 32, softmax_scale: Optional[float] = None,
-                        out=None, workspace=None, stream=None, _bf16pv=False):
+                        out=None, workspace=None, stream=None, _bf16pv=False, _uint8w=False):
     """Chunked prefill with history; returns ``out`` [total_q, Hq, D] fp32."""
     import torch
     lib = load_library()
@@ -655,10 +658,26 @@ def prefix_prefill_int8(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_l
     if _bf16pv:
         st = lib.i8kv_prefix_prefill_bf16pv(*common, *tail)
         _raise("prefix_prefill_bf16pv", st)
+    elif _uint8w:
+        st = lib.i8kv_prefix_prefill_uint8w(*common, int(w_group), *tail)
+        _raise("prefix_prefill_uint8w", st)
     else:
         st = lib.i8kv_prefix_prefill_int8(*common, int(w_group), *tail)
         _raise("prefix_prefill_int8", st)
     return out
+
+
+@_allocates_on_stream
+def prefix_prefill_uint8w(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_lens,
+                          cache: PagedCache, block_tables, max_query_len: int, w_group: int = 32,
+                          softmax_scale: Optional[float] = None, out=None, workspace=None,
+                          stream=None):
+    """The UINT8-W variant of prefix_prefill_int8 (W groups quantized to
+    0..255 against max W / 255); same arguments."""
+    return prefix_prefill_int8(desc, q_int8, q_scale, query_start_loc, seq_lens, cache,
+                               block_tables, max_query_len, w_group=w_group,
+                               softmax_scale=softmax_scale, out=out, workspace=workspace,
+                               stream=stream, _uint8w=True)
 
 
 @_allocates_on_stream

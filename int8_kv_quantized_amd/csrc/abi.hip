@@ -117,7 +117,7 @@ i8kv_status run_prefill(const i8kv_cache_desc* desc, int32_t num_seqs,
                                      int32_t w_group, float softmax_scale, void* workspace,
                                      size_t workspace_bytes, float* out,
                                      i8kv_stream_t stream, bool pv_bf16,
-                                     const uint16_t* q_bf16 = nullptr) {
+                                     const uint16_t* q_bf16 = nullptr, bool w_uint8 = false) {
   (void)workspace;
   (void)workspace_bytes;
   i8kv_status st = check_desc(desc);
@@ -147,6 +147,7 @@ i8kv_status run_prefill(const i8kv_cache_desc* desc, int32_t num_seqs,
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.w_group = w_group;
   a.pv_bf16 = pv_bf16 ? 1 : 0;
+  a.w_uint8 = w_uint8 ? 1 : 0;
   a.softmax_scale = softmax_scale;
   a.q_int8 = q_bf16 ? nullptr : q_int8;
   a.q_scale = q_bf16 ? nullptr : q_scale;
@@ -537,6 +538,22 @@ i8kv_status i8kv_prefix_prefill_int8(const i8kv_cache_desc* desc, int32_t num_se
                      seq_lens, k_cache, v_cache, k_scale, v_scale, block_tables,
                      max_blocks_per_seq, w_group, softmax_scale, workspace, workspace_bytes, out,
                      stream, false);
+}
+
+i8kv_status i8kv_prefix_prefill_uint8w(const i8kv_cache_desc* desc, int32_t num_seqs,
+                                       int32_t total_q, int32_t max_query_len,
+                                       const int8_t* q_int8, const float* q_scale,
+                                       const int32_t* query_start_loc, const int32_t* seq_lens,
+                                       const int8_t* k_cache, const int8_t* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       int32_t w_group, float softmax_scale, void* workspace,
+                                       size_t workspace_bytes, float* out,
+                                       i8kv_stream_t stream) {
+  return run_prefill(desc, num_seqs, total_q, max_query_len, q_int8, q_scale, query_start_loc,
+                     seq_lens, k_cache, v_cache, k_scale, v_scale, block_tables,
+                     max_blocks_per_seq, w_group, softmax_scale, workspace, workspace_bytes, out,
+                     stream, false, nullptr, /*w_uint8=*/true);
 }
 
 i8kv_status i8kv_prefix_prefill_bf16pv(const i8kv_cache_desc* desc, int32_t num_seqs,

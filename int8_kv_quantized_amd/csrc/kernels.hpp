@@ -87,6 +87,7 @@ struct PrefillArgs {
   int32_t num_seqs, total_q, max_query_len, num_q_heads, num_kv_heads, group, head_dim,
       num_blocks, max_blocks_per_seq, w_group;
   int32_t pv_bf16;  // the BF16-PV ablation (w_group unused)
+  int32_t w_uint8;  // UINT8 W groups (codes 0..255, sW = max W / 255)
   float softmax_scale;
   const int8_t* q_int8;
   const float* q_scale;

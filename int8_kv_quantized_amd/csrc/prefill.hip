@@ -142,7 +142,10 @@ struct PrefillTile {
 // int8 K codes taken exactly as bf16: each K tile, once landed, is converted
 // to bf16 in LDS by the whole workgroup, and S^T = K Q^T runs on
 // v_mfma_f32_16x16x32_bf16 with fp32 accumulation; score = dot * sK * scale.
-template <int D, int G, bool BPV, bool QB>
+// U8W: UINT8 W groups (sW = max W / 255, codes 0..255 passed to the signed
+// MFMA as c - 128; a second MFMA against all-ones gives each group's sum of V,
+// and 128 times it is added back in int32, exactly).
+template <int D, int G, bool BPV, bool QB, bool U8W = false>
 __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_kernel(
     PrefillArgs a) {
   constexpr int kNW = PrefillShape<QB>::NW;
@@ -413,23 +416,62 @@ __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_k
       return;
     }
     if constexpr (G == 64) am[0] = am[1] = fmaxf(am[0], am[1]);
+    constexpr float kQmax = U8W ? 255.0f : 127.0f;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      swg[g] = am[g] * (1.0f / 127.0f);
-      // 127 / max W; W * inv + 0.5 stays below 128 since W <= max W and the
-      // reciprocal is within an ulp, so truncation gives round-half-up in [0, 127]
-      const float inv = am[g] > 0.0f ? 127.0f * __builtin_amdgcn_rcpf(am[g]) : 0.0f;
+      swg[g] = am[g] * (1.0f / kQmax);
+      // inv = kQmax / max W (hardware reciprocal, within an ulp); the code is
+      // W * inv rounded to the nearest integer by the byte conversion itself
+      // (nearest-even on an exact tie, saturating at 255, so W <= max W stays
+      // in [0, kQmax]): one instruction per code for the multiply and one for
+      // round-and-pack
+      const float inv = am[g] > 0.0f ? kQmax * __builtin_amdgcn_rcpf(am[g]) : 0.0f;
       uint32_t pk[2] = {0, 0};
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        pk[j >> 2] |= (uint32_t)__builtin_fmaf(Wv[g][j], inv, 0.5f) << (8 * (j & 3));
-      wpk[g][0] = pk[0];
-      wpk[g][1] = pk[1];
+        pk[j >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(Wv[g][j] * inv, j & 3, pk[j >> 2]);
+      wpk[g][0] = U8W ? pk[0] ^ 0x80808080u : pk[0];  // UINT8: c - 128 as int8
+      wpk[g][1] = U8W ? pk[1] ^ 0x80808080u : pk[1];
     }
     // ---- O^T += sW * (V^T Wq^T) --------------------------------------------------
     const int8_t* vt = s_v[buf];
     const int voff = 8 * (lg & 1);
-    if constexpr (G == 32) {
+    if constexpr (U8W) {
+      // per group: C = V^T (Wq - 128)^T, CS = V^T 1 (the group's sum of V per
+      // dim, the same for every row), O += sW * float(C + 128 CS)
+      const long ones8 = 0x0101010101010101L;
+      const v4i ones16 = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+      const long wb0 = (long)(((uint64_t)wpk[0][1] << 32) | wpk[0][0]);
+      const long wb1 = (long)(((uint64_t)wpk[1][1] << 32) | wpk[1][0]);
+      const v4i wb = {(int)wpk[0][0], (int)wpk[0][1], (int)wpk[1][0], (int)wpk[1][1]};
+      const int8_t* vp0 = vt + ((lg >> 1) * D + lr) * 16 + voff;
+      const int8_t* vp1 = vt + ((2 + (lg >> 1)) * D + lr) * 16 + voff;
+      const v4i z = {0, 0, 0, 0};
+#pragma unroll
+      for (int n = 0; n < NN; ++n) {
+        const long va0 = *reinterpret_cast<const long*>(vp0 + 256 * n);
+        const long va1 = *reinterpret_cast<const long*>(vp1 + 256 * n);
+        if constexpr (G == 32) {
+          const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(va0, wb0, z, 0, 0, 0);
+          const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(va1, wb1, z, 0, 0, 0);
+          const v4i s0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(va0, ones8, z, 0, 0, 0);
+          const v4i s1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(va1, ones8, z, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            O[n][i] = __builtin_fmaf(swg[0], (float)(c0[i] + (s0[i] << 7)), O[n][i]);
+            O[n][i] = __builtin_fmaf(swg[1], (float)(c1[i] + (s1[i] << 7)), O[n][i]);
+          }
+        } else {
+          const v4i va = {(int)(uint32_t)va0, (int)(uint32_t)((uint64_t)va0 >> 32),
+                          (int)(uint32_t)va1, (int)(uint32_t)((uint64_t)va1 >> 32)};
+          const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(va, wb, z, 0, 0, 0);
+          const v4i cs = __builtin_amdgcn_mfma_i32_16x16x64_i8(va, ones16, z, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            O[n][i] = __builtin_fmaf(swg[0], (float)(c[i] + (cs[i] << 7)), O[n][i]);
+        }
+      }
+    } else if constexpr (G == 32) {
       // Both groups of the tile in one pass, the int32 -> fp32 conversion done
       // by the MFMA: its accumulator starts at the bit pattern of kMagic, so
       // the result read as fp32 is exactly kMagic + acc (|acc| <= 32 * 127^2 <
@@ -554,6 +596,9 @@ hipError_t launch_prefix_prefill(const PrefillArgs& a, hipStream_t stream) {
     else if (a.pv_bf16)                                                                        \
       hipLaunchKernelGGL((prefix_prefill_kernel<DD, GG, true, false>), grid, block, 0, stream, \
                          a);                                                                   \
+    else if (a.w_uint8)                                                                        \
+      hipLaunchKernelGGL((prefix_prefill_kernel<DD, GG, false, false, true>), grid, block, 0,  \
+                         stream, a);                                                           \
     else                                                                                       \
       hipLaunchKernelGGL((prefix_prefill_kernel<DD, GG, false, false>), grid, block, 0,        \
                          stream, a);                                                           \

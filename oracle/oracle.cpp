@@ -561,6 +561,7 @@ int prefill_row_impl(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
                          : Query{q_int8 + qr * D, q_scale[qr], nullptr};
   const bool exact = (flags & ORC_EXACT) != 0;
   const bool bf16_pv = (flags & ORC_BF16_PV) != 0;
+  const bool u8_w = (flags & ORC_UINT8_W) != 0;
   const bool quant_w = (flags & ORC_NO_WQUANT) == 0 && !bf16_pv;
 
   /* [PV 2.1] online softmax over key tiles: state (m, l, o). */
@@ -614,7 +615,12 @@ int prefill_row_impl(int Hq, int Hkv, int D, int bs, int nb, int S, int Tq,
     for (int d = 0; d < D; ++d) o[d] *= (double)alpha;
     for (int g0 = 0; g0 < n; g0 += w_group) {
       const int gn = std::min(w_group, n - g0);
-      if (quant_w) {
+      if (quant_w && u8_w) {
+        /* [PV 6] the UINT8 candidate: W >= 0, so 0..255 against max W / 255 */
+        add_group_quantized_u8(&W[g0], t0 + g0, gn, sv, D, 1.0, o.data(),
+                               tr && tr->Wq ? tr->Wq + t0 + g0 : nullptr,
+                               tr && tr->sW ? tr->sW + (t0 + g0) / w_group : nullptr);
+      } else if (quant_w) {
         add_group_quantized(&W[g0], t0 + g0, gn, sv, D, 1.0, o.data(),
                             tr && tr->Wq ? tr->Wq + t0 + g0 : nullptr,
                             tr && tr->sW ? tr->sW + (t0 + g0) / w_group : nullptr);

@@ -45,9 +45,9 @@ enum {
                         p~ * sV) rounded to bf16 (nearest, ties to even)
                         instead of group-quantized to int8, times the int8 V
                         (exact products, fp64 sum); everything else unchanged */
-  ORC_UINT8_W = 8    /* decode only: W groups quantized to UINT8 (sW = max W /
-                        255, Wq in [0, 255]); the trace's Wq holds the uint8
-                        codes */
+  ORC_UINT8_W = 8    /* W groups quantized to UINT8 (sW = max W / 255, Wq in
+                        [0, 255]), decode and prefill; the trace's Wq holds
+                        the uint8 codes */
 };
 
 /* Symmetric int8 quantization of one vector [KV 2.1]:

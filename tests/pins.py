@@ -846,6 +846,69 @@ def pin_prefill_bf16_pv(orc, seed=17, tile=64):
             assert np.all(np.abs(tb["out"] - ref[r, h]) <= bound), "bf16-PV prefill above bound"
 
 
+def pin_prefill_uint8_w(orc, G=32, seed=20, tile=64):
+    """The UINT8-W prefill (the PV-MMAC page's section 6 candidate in the
+    prefill's online softmax): scores, running maxima, p~ and l equal the int8
+    path's; per aligned group sW = max W / 255 bit for bit and Wq the
+    brute-force nearest codes of W / sW over 0..255; the output equals the
+    re-assembly sum c_tok sW Wq Vq / l and stays within the bound against fp64
+    causal attention with the sW / 2 term; on average it is closer to fp64
+    attention than int8 W."""
+    from oracle import ORC_UINT8_W
+    wl = tiny_prefill(seed=seed)
+    cache, q8, qs = orc.fill(wl)
+    K, V, sK, sV = cache_rows(cache)
+    grp = wl.num_q_heads // wl.num_kv_heads
+    ref = prefill_reference_fp64(wl)
+    args = (q8, qs, wl.query_start_loc, wl.seq_lens, cache, wl.block_tables)
+    err_u = err8 = 0.0
+    for r, b, pos in _prefill_rows(wl)[::3]:
+        for h in range(0, wl.num_q_heads, 2):
+            kv = h // grp
+            tu = orc.prefill_row(*args, r, h, w_group=G, tile=tile, flags=ORC_UINT8_W)
+            t8 = orc.prefill_row(*args, r, h, w_group=G, tile=tile)
+            for k in ("s", "ptil", "m_tile", "l"):
+                assert np.array_equal(tu[k], t8[k]), f"uint8-W prefill changed {k}"
+            nk = pos + 1
+            sl = seq_slots(wl, b)[:nk]
+            w32 = (tu["ptil"] * sV[sl, kv]).astype(np.float32)
+            wq = tu["Wq"].view(np.uint8).astype(np.int64)
+            for g0 in range(0, nk, G):
+                g1 = min(nk, g0 + G)
+                w = w32[g0:g1]
+                sw = tu["sW"][g0 // G]
+                exp_sw = np.float32(w.max()) / np.float32(255) if w.max() > 0 else np.float32(0)
+                assert sw.view(np.uint32) == np.float32(exp_sw).view(np.uint32), "group sW"
+                if sw > 0:
+                    assert np.array_equal(wq[g0:g1], nearest_code_u8((w / sw).astype(np.float32))), \
+                        "group codes"
+                else:
+                    assert not wq[g0:g1].any()
+            m_of = np.zeros(nk)
+            for ti, t0 in enumerate(range(0, nk, tile)):
+                m_of[t0:min(nk, t0 + tile)] = float(tu["m_tile"][ti])
+            c_tok = np.exp(m_of - m_of[-1])
+            sW_tok = np.repeat(tu["sW"].astype(np.float64), G)[:nk]
+            vq = V[sl, kv].astype(np.float64)
+            o = (c_tok * sW_tok * wq) @ vq
+            l = float(tu["l"][0])
+            assert np.all(np.abs(tu["out"] - o / l) <= 1e-5 * (np.abs(o / l) + 1e-3)), \
+                "o/l re-assembly"
+            tok = np.nonzero(wl.token_seq == b)[0]
+            tok = tok[np.argsort(wl.token_pos[tok])][:nk]
+            Vorig = W.bf16_bits_to_f32(wl.value[tok, kv]).astype(np.float64)
+            Korig = W.bf16_bits_to_f32(wl.key[tok, kv]).astype(np.float64)
+            qorig = W.bf16_bits_to_f32(wl.query[r, h]).astype(np.float64)
+            Pe = _softmax64(Korig @ qorig / np.sqrt(wl.head_dim))
+            P = c_tok * tu["ptil"] / l
+            bound = (np.abs(Pe - P) @ np.abs(Vorig) + (P * sV[sl, kv] / 2).sum()
+                     + (c_tok * sW_tok / l / 2 * (1 + 1e-6)) @ np.abs(vq) + 1e-5)
+            assert np.all(np.abs(tu["out"] - ref[r, h]) <= bound), "uint8-W prefill above bound"
+            err_u += np.abs(tu["out"] - ref[r, h]).mean()
+            err8 += np.abs(t8["out"] - ref[r, h]).mean()
+    assert err_u < err8, f"uint8 W not more accurate on average ({err_u} vs {err8})"
+
+
 def pin_prefill_vs_decode(orc, G=32, seed=9):
     """A prefill row equals a decode of the same query over its visible keys
     (exactly in real arithmetic; here up to fp32 rounding)."""
@@ -961,4 +1024,4 @@ ALL_PINS = [pin_quantize_golden, pin_quantize_bruteforce, pin_cache_layout,
             pin_prefill_vs_decode, pin_rope_rotation, pin_rope_producer,
             pin_bf16_rounding, pin_decode_bf16_pv, pin_quantize_w_u8, pin_decode_uint8_w,
             pin_decode_multi_query, pin_prefill_bf16_pv, pin_decode_bf16_qk,
-            pin_prefill_bf16_qk]
+            pin_prefill_bf16_qk, pin_prefill_uint8_w]

@@ -28,7 +28,9 @@ def test_header_declares_the_operations():
     for op in ("i8kv_kv_quantize_write", "i8kv_kv_quantize_write_rope", "i8kv_paged_decode_int8",
                "i8kv_paged_decode_bf16pv", "i8kv_paged_decode_uint8w", "i8kv_paged_decode_ex",
                "i8kv_prefix_prefill_int8", "i8kv_prefix_prefill_bf16pv", "i8kv_decode_step_int8",
-               "i8kv_paged_decode_bf16qk", "i8kv_prefix_prefill_bf16qk"):
+               "i8kv_paged_decode_bf16qk", "i8kv_prefix_prefill_bf16qk",
+               "i8kv_paged_decode_partials", "i8kv_paged_decode_merge",
+               "i8kv_prefix_prefill_uint8w", "i8kv_paged_decode_int8_noalloc"):
         assert op in names
 
 
@@ -385,3 +387,24 @@ def test_noalloc_decode_size_checks_before_any_device_call():
     assert K.paged_decode_workspace_bytes(d, 32, 32768) > 64 << 20
     assert lib.i8kv_paged_decode_int8_noalloc(*args(d, 32, 32768)) == WORKSPACE
     assert K.paged_decode_workspace_bytes(d, 16, 32768) <= 64 << 20
+
+
+def test_prefill_uint8w_validation():
+    """The UINT8-W prefill validates as the int8 prefill does, before any launch."""
+    P = lambda x: None if x is None else C.c_void_p(x)
+    lib = _lib()
+
+    def call(d, S=1, Tq=8, max_q=8, G=32, q8=FAKE, qsl=FAKE, scale=0.0625):
+        return lib.i8kv_prefix_prefill_uint8w(
+            None if d is None else C.byref(d), S, Tq, max_q, P(q8), P(FAKE), P(qsl), P(FAKE),
+            P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 32, G, scale, None, 0, P(FAKE), None)
+    assert call(None) == NULL
+    assert call(desc(D=100)) == UNSUPPORTED
+    assert call(desc(), q8=None) == NULL
+    assert call(desc(), qsl=None) == NULL
+    assert call(desc(), G=48) == UNSUPPORTED
+    assert call(desc(), S=-1) == INVALID
+    assert call(desc(), max_q=9) == INVALID
+    assert call(desc(), scale=float("inf")) == INVALID
+    assert call(desc(), q8=FAKE + 4) == INVALID
+    assert call(desc(), S=0) == OK

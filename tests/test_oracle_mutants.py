@@ -64,7 +64,10 @@ MUTANTS = {
     "u8_clamp_127": [("    if (r > 255.0f) r = 255.0f;", "    if (r > 127.0f) r = 127.0f;")],
     "u8_round_down": [("    float r = std::round(w[i] / s);\n    if (r > 255.0f)",
                        "    float r = std::floor(w[i] / s);\n    if (r > 255.0f)")],
-    "u8_flag_ignored": [("      if (quant_w && u8_w) {", "      if (false) {")],
+    "u8_flag_ignored": [("      if (quant_w && u8_w) {\n        add_group_quantized_u8(&W[g0], i0 + g0",
+                         "      if (false) {\n        add_group_quantized_u8(&W[g0], i0 + g0")],
+    "prefill_u8_flag_ignored": [("      if (quant_w && u8_w) {\n        /* [PV 6]",
+                                 "      if (false) {\n        /* [PV 6]")],
     "prefill_bf16_ignored": [("      if (bf16_pv) W[j] = round_to_bf16(W[j]);", "")],
     "prefill_bf16_before_sv": [("      if (bf16_pv) W[j] = round_to_bf16(W[j]);",
                                 "      if (bf16_pv) W[j] = round_to_bf16(pt[j]) * sv.sv(t0 + j);")],

@@ -12,7 +12,8 @@ def test_pin_g32(orc, pin):
 
 @pytest.mark.parametrize("pin", [pins.pin_decode_trace, pins.pin_decode_bruteforce,
                                  pins.pin_decode_partition_invariance,
-                                 pins.pin_prefill_trace, pins.pin_prefill_vs_decode],
+                                 pins.pin_prefill_trace, pins.pin_prefill_vs_decode,
+                                 pins.pin_prefill_uint8_w],
                          ids=lambda f: f.__name__)
 def test_pin_g64(orc, pin):
     pin(orc, G=64)

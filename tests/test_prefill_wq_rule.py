@@ -4,8 +4,9 @@ The definition ("Implementing INT8 PV MMAC on a gfx936 DCU", section 1):
 sW = max W / 127 and Wq = round(W / sW), an IEEE fp32 division with ties
 away from zero.  The prefill kernel instead multiplies: inv = 127 * r with r
 the hardware reciprocal of max W (within one unit in the last place of
-1 / max W), and Wq = trunc(fma(W, inv, 0.5)).  The two can differ by one code
-where W / sW lies next to a half-integer.
+1 / max W), and Wq = the fp32 product W * inv rounded to the nearest integer
+by the byte conversion (ties to even).  The two can differ by one code where
+W / sW lies next to a half-integer.
 
 On a sample of the 2048-over-16384 chunk (rows at row-tile ends, all 24
 heads, the oracle's own W = p~ sV of every visible key, aligned 32-key
@@ -23,11 +24,8 @@ import workloads as W
 
 def kernel_codes(w, am, r):
     inv = np.float32(np.float32(127.0) * np.float32(r))
-    # fma(W, inv, 0.5) rounded once to fp32: the fp64 value of W * inv is
-    # exact (two 24-bit significands), the + 0.5 leaves at most one fp64
-    # rounding far below fp32 precision
-    x = (w.astype(np.float64) * np.float64(inv) + 0.5).astype(np.float32)
-    return np.trunc(x).astype(np.int64)
+    x = (w * inv).astype(np.float32)           # the fp32 product
+    return np.rint(x).astype(np.int64)          # nearest, ties to even
 
 
 def ieee_codes(w, am):
