@@ -599,9 +599,10 @@ DECODE_SOURCES = ["int8_kv_quantized_amd/csrc/decode.hip", "int8_kv_quantized_am
 
 
 def counted_traffic(workload, G):
-    """HBM bytes per decode call from the committed FETCH_SIZE / WRITE_SIZE
-    counters (profiles/hbm_traffic.json), or None when no record matches the
-    workload or the decode kernel sources changed since they were taken."""
+    """HBM bytes per launch of the decode's partition kernel from the committed
+    FETCH_SIZE / WRITE_SIZE counters (profiles/hbm_traffic.json), or None when
+    no record matches the workload or the decode kernel sources changed since
+    they were taken."""
     import hashlib
     path = ROOT / "profiles" / "hbm_traffic.json"
     if not path.exists():
@@ -612,8 +613,9 @@ def counted_traffic(workload, G):
     for rec in json.loads(path.read_text()):
         if (rec.get("workload") == workload and rec.get("w_group") == G
                 and rec.get("kernel_sources") == DECODE_SOURCES
-                and rec.get("kernel_sources_sha256") == h.hexdigest()):
-            return int(rec["hbm_bytes_per_call"])
+                and rec.get("kernel_sources_sha256") == h.hexdigest()
+                and "hbm_bytes_per_launch" in rec):
+            return int(rec["hbm_bytes_per_launch"])
     return None
 
 
