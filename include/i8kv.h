@@ -1,7 +1,7 @@
 /*
  * i8kv -- paged attention over an INT8 KV cache, native to AMD MI355X (gfx950).
  *
- * C ABI of the library libi8kv.so.  Eleven calls, on the operations defined on the pages
+ * C ABI of the library libi8kv.so.  Fifteen calls, on the operations defined on the pages
  *   [KV] "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
  *        DCU" (part 1 of the series), and
  *   [PV] "Implementing INT8 PV MMAC on a gfx936 DCU: V-scale fusion,
@@ -12,6 +12,11 @@
  *                              embedding of Q and K fused in ([KV] 2.2)
  *   i8kv_paged_decode_int8  -- decode over 256-token partitions ([KV] 3.3,
  *                              [PV] 2.2, merge by log-sum-exp weights)
+ *   i8kv_paged_decode_partials, i8kv_paged_decode_merge -- the decode's two
+ *                              stages as separate calls (partitions, then the
+ *                              merge of their partials; [PV] 2.2)
+ *   i8kv_paged_decode_int8_noalloc -- the decode for callers that cannot
+ *                              allocate (partials in a fixed per-GPU array)
  *   i8kv_prefix_prefill_int8 -- chunked prefill with history in one online
  *                              softmax ([KV] 3.2, [PV] 2.1)
  *   i8kv_decode_step_int8   -- the producer of each sequence's newest token
@@ -26,12 +31,16 @@
  *   i8kv_paged_decode_bf16qk -- the decode with a bf16 QK product (the
  *                              pages' QK comparison, [KV] 4.1)
  *   i8kv_prefix_prefill_bf16qk -- the prefill with a bf16 QK product ([KV] 4.1)
+ *   i8kv_prefix_prefill_uint8w -- the prefill with UINT8 W groups ([PV] 6)
+ * plus the workspace-size queries, i8kv_status_string and i8kv_abi_version.
  *
  * Conventions for every call
  *  - Tensor arguments are DEVICE pointers owned by the caller, C-contiguous in
  *    the layouts given below.  The library never allocates, frees or
  *    synchronizes, keeps no global state and is re-entrant; all work is
  *    enqueued on `stream` (NULL = the default stream) and is asynchronous.
+ *    The one exception is i8kv_paged_decode_int8_noalloc, whose fixed device
+ *    array per GPU is shared by every call on that GPU (see there).
  *  - bf16 tensors are passed as their 16-bit patterns (uint16_t).
  *  - Cache layouts ([KV] 2.3), with x = 16 head-dim bytes per token:
  *      k_cache [num_blocks, Hkv, D/16, block_size, 16]  int8
