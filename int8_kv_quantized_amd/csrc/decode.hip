@@ -580,17 +580,22 @@ paged_decode_partition_kernel(
 // One wave per (q head, sequence, 32-dim slice), no barriers:
 //   O = sum_p w_p o_p / sum_p w_p, w_p = l_p exp(m_p - M), M = max_p m_p.
 // Lane l owns float4 column l % 8 of the 32-dim slice for partitions
-// p = l / 8 (mod 8), U per round; the partial loads of the first round and
-// lane l's (m_l, l_l) go out before the sequence length is known (every slot
-// below max_parts exists in the workspace; slots past the sequence are
-// discarded).  The weight of partition p is computed by lane p % 64 and
-// fetched with a cross-lane read; the eight lane groups are summed with two
-// swaps and one xor exchange.  (32 rather than 64 dims per wave: twice the
-// waves, half the loads per lane -- 1% faster at 16K, 1.2% at 32K.)
-template <int D>
+// p = l / 8 (mod 8), U per round (RP = 8 U partitions per round: 64, or 128
+// when the call has more than 64); the partial loads of the first round and
+// the (m, l) of partitions l, l + 64, ... of the first round go out before the
+// sequence length is known (every slot below max_parts exists in the
+// workspace; slots past the sequence are discarded), so a sequence of up to
+// RP partitions costs one memory round trip.  The weight of partition p is
+// computed by lane p % 64 and fetched with a cross-lane read; the eight lane
+// groups are summed with two swaps and one xor exchange.  (32 rather than 64
+// dims per wave: twice the waves, half the loads per lane -- 1% faster at
+// 16K, 1.2% at 32K.)  Every lane adds its partitions in increasing order
+// whatever U is, so U does not change the result.
+template <int D, int U>
 __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a) {
-  constexpr int U = 8;            // partitions per lane per round
-  constexpr int RP = 8 * U;        // partitions per round (= 64)
+  constexpr int RP = 8 * U;        // partitions per round
+  constexpr int NML = RP / kWave;  // (m, l) pairs per lane per round
+  static_assert(RP % kWave == 0, "a round covers whole waves of partitions");
   // blockIdx.x = qi * Hq + h: query qi (of nq) of the sequence, q head h
   const int qi = blockIdx.x / a.num_q_heads, h = blockIdx.x % a.num_q_heads;
   const int s = blockIdx.y, slice = blockIdx.z, lane = threadIdx.x;
@@ -610,7 +615,9 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
     }
   };
   issue(0);
-  const float2 ml0 = ml[(size_t)min(lane, a.max_parts - 1) * rows];
+  float2 ml0[NML];
+#pragma unroll
+  for (int k = 0; k < NML; ++k) ml0[k] = ml[(size_t)min(lane + kWave * k, a.max_parts - 1) * rows];
   int L = a.seq_lens[s];
   L = min(max(L, 0), a.max_seq_len);
   const int P_s = (L + kPartition - 1) / kPartition;
@@ -634,19 +641,27 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
     return;
   }
 
-  float m = lane < P_s ? ml0.x : -INFINITY;
-  for (int q = lane + RP; q < P_s; q += RP) m = fmaxf(m, ml[(size_t)q * rows].x);
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NML; ++k)
+    if (lane + kWave * k < P_s) m = fmaxf(m, ml0[k].x);
+  for (int q = lane + RP; q < P_s; q += kWave) m = fmaxf(m, ml[(size_t)q * rows].x);
   const float M = group_max<kWave>(m);
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float wsum = 0.0f;
   for (int q0 = 0; q0 < P_s; q0 += RP) {
-    float wl = 0.0f;  // weight of partition q0 + lane
-    if (q0 + lane < P_s) {
-      const float2 e = q0 == 0 ? ml0 : ml[(size_t)(q0 + lane) * rows];
-      wl = e.y > 0.0f ? e.y * expf(e.x - M) : 0.0f;  // l = 0: a partition this query does not see
+    float wl[NML];  // weight of partition q0 + lane + 64 k
+#pragma unroll
+    for (int k = 0; k < NML; ++k) {
+      const int q = q0 + lane + kWave * k;
+      wl[k] = 0.0f;
+      if (q < P_s) {
+        const float2 e = q0 == 0 ? ml0[k] : ml[(size_t)q * rows];
+        wl[k] = e.y > 0.0f ? e.y * expf(e.x - M) : 0.0f;  // l = 0: a partition this query does not see
+      }
+      wsum += wl[k];
     }
-    wsum += wl;
     if (q0 > 0) issue(q0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -654,7 +669,7 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
       // known) but never written: whatever they hold, even NaN or Inf, is
       // dropped by the select, not multiplied by a zero weight.
       const bool live = q0 + lg + 8 * u < P_s;
-      const float wq = __shfl(wl, lg + 8 * u, kWave);
+      const float wq = __shfl(wl[(8 * u) / kWave], (lg + 8 * u) % kWave, kWave);
       acc.x += live ? wq * v[u].x : 0.0f;
       acc.y += live ? wq * v[u].y : 0.0f;
       acc.z += live ? wq * v[u].z : 0.0f;
@@ -679,6 +694,18 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
   }
 }
 
+// The merge with one round per 64 partitions (U = 8) or per 128 (U = 16).
+// The wider round pays off for one long sequence (32K: 20.4 -> 19.9 us per
+// call); in a batch, sequences shorter than max_parts would load slots they do
+// not have in the first round (batch 16 at L ~ U[1K, 32K]: 132.8 -> 134.1 us).
+template <int D>
+void launch_merge(const DecodeArgs& a, dim3 mgrid, hipStream_t stream) {
+  if (a.max_parts > 64 && a.num_seqs == 1)
+    hipLaunchKernelGGL((paged_decode_merge_kernel<D, 16>), mgrid, dim3(kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((paged_decode_merge_kernel<D, 8>), mgrid, dim3(kWave), 0, stream, a);
+}
+
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
   dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
@@ -688,7 +715,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     const dim3 blk(DecodeShape<DD>::NW * kWave);                                                 \
     const bool mq = a.nq > 1;                                                                    \
     if (a.stage == 2) {                                                                          \
-      hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(kWave), 0, stream, a);     \
+      launch_merge<DD>(a, mgrid, stream);                                                        \
       return hipGetLastError();                                                                  \
     }                                                                                            \
     if (a.new_key)                                                                               \
@@ -716,7 +743,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false, false>),  \
                          grid, blk, 0, stream, a);                                               \
     if (a.max_parts > 1 && a.stage == 0)                                                         \
-      hipLaunchKernelGGL((paged_decode_merge_kernel<DD>), mgrid, dim3(kWave), 0, stream, a);     \
+      launch_merge<DD>(a, mgrid, stream);                                                        \
     return hipGetLastError();                                                                    \
   }
   I8KV_DECODE_CASE(64, 32)

@@ -50,6 +50,31 @@ def test_partials_then_merge_equal_the_call(orc, G):
     assert_close(two, ref, f"{wl.name} G={G} stages")
 
 
+def test_partials_then_merge_equal_the_call_32k(orc):
+    """One 32768-token sequence: 128 partitions, merged in one 128-partition
+    round (the batch-1 merge); the merge alone equals the call bit for bit."""
+    import int8_kv_quantized_amd as K
+    import torch
+    wl = W.cfg3_decode_32k()
+    say(f"  stages case {wl.name}")
+    d, cache, q8, qs = gpu_fill(wl)
+    dq8, dqs = decode_queries(q8, qs, wl)
+    bt, sl, L = dev(wl.block_tables), dev(wl.seq_lens), wl.max_seq_len
+    nbytes = K.paged_decode_workspace_bytes(d, wl.num_seqs, L)
+    ws = torch.full(((nbytes + 3) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    one = K.paged_decode_int8(d, dq8, dqs, cache, bt, sl, L, w_group=32)
+    K.paged_decode_partials(d, dq8, dqs, cache, bt, sl, L, w_group=32, workspace=ws)
+    two = K.paged_decode_merge(d, sl, L, ws)
+    torch.cuda.synchronize()
+    one, two = one.cpu().numpy(), two.cpu().numpy()
+    assert_bits_equal(two, one, "partials + merge vs one call (32K)")
+    ocache, oq8, oqs = orc.fill(wl)
+    rows = wl.decode_query_rows()
+    ref = orc.paged_decode(oq8[rows], oqs[rows], ocache, wl.block_tables, wl.seq_lens,
+                           num_q_heads=wl.num_q_heads, w_group=32)
+    assert_close(two, ref, f"{wl.name} stages")
+
+
 @pytest.mark.parametrize("cuts", [(4096,), (2048, 8192, 12288)], ids=["2shards", "4shards"])
 def test_decode_sharded_over_partitions(orc, cuts):
     """16384 tokens (the 16K configuration) cut into shards at multiples of 256."""

@@ -5,7 +5,8 @@ Every decode entry point is run over a workspace filled with NaN, then with
 are the ones where the merge meets workspace slots that the partition kernel
 never writes: ragged batches (a short sequence next to a long one), a batch-1
 call whose max_seq_len lies several partitions past seq_lens[0], several
-queries per sequence, the fused step, and every PV/QK variant.  The merge of
+queries per sequence, the fused step, every PV/QK variant, and a batch-1
+call long enough for the merge's 128-partition rounds.  The merge of
 partition outputs with log-sum-exp weights follows the page "Implementing
 INT8 PV MMAC on a gfx936 DCU", section 2.2: only a sequence's own partitions
 enter its sum.
@@ -43,6 +44,13 @@ def batch1_short(G=32):
                            num_kv_heads=4, head_dim=256, seed=92, w_group=G)
 
 
+def batch1_long(G=32):
+    """67 partitions: a batch-1 call with more than 64 partitions merges 128 per
+    round, whose first round loads slots 67 .. 127 before the length is known."""
+    return W.make_workload("poison_batch1_long", seq_lens=(17000,), new_tokens=(1,),
+                           num_q_heads=24, num_kv_heads=4, head_dim=256, seed=97, w_group=G)
+
+
 def decode_case(wl, orc, fill, G=32, extra_parts=0):
     import int8_kv_quantized_amd as K
     import torch
@@ -78,6 +86,13 @@ def test_poisoned_cfg5_mha(orc, fill, G):
 @pytest.mark.parametrize("G", [32, 64])
 def test_poisoned_batch1_max_len_past_sequence(orc, fill, G):
     decode_case(batch1_short(G), orc, fill, G=G, extra_parts=5)
+
+
+@pytest.mark.parametrize("fill", list(FILLS))
+def test_poisoned_batch1_long_two_merge_rounds(orc, fill):
+    """max_seq_len 70 partitions past the sequence: 137 workspace slots, two
+    128-partition merge rounds, every slot from 67 on never written."""
+    decode_case(batch1_long(), orc, fill, extra_parts=70)
 
 
 @pytest.mark.parametrize("fill", list(FILLS))
