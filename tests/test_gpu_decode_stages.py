@@ -50,6 +50,49 @@ def test_partials_then_merge_equal_the_call(orc, G):
     assert_close(two, ref, f"{wl.name} G={G} stages")
 
 
+@pytest.mark.parametrize("G", [32, 64])
+def test_batched_call_equals_one_call_per_sequence(orc, G):
+    """A batch of eight sequences (empty, one-partition and up to 128-partition
+    ones) against each sequence decoded alone: bit for bit.  Alone, a
+    sequence of more than 64 partitions is merged in 128-partition rounds,
+    in the batch in 64-partition rounds; every lane adds its partitions in
+    the same order either way.  The batch's partials + merge equal the batched
+    call, and the oracle agrees within tolerance."""
+    import int8_kv_quantized_amd as K
+    import torch
+    wl = W.make_workload("batch_vs_alone", seq_lens=(20000, 1, 256, 32768, 257, 9000, 600, 31000),
+                         new_tokens=[1] * 8, num_q_heads=24, num_kv_heads=4, head_dim=256,
+                         seed=96, w_group=G)
+    say(f"  batch vs one call per sequence {wl.name} G={G}")
+    d, cache, q8, qs = gpu_fill(wl)
+    dq8, dqs = decode_queries(q8, qs, wl)
+    lens = wl.seq_lens.astype(np.int32).copy()
+    lens[4] = 0  # an empty sequence
+    bt, sl, L = dev(wl.block_tables), dev(lens), wl.max_seq_len
+    one = K.paged_decode_int8(d, dq8, dqs, cache, bt, sl, L, w_group=G)
+    nbytes = K.paged_decode_workspace_bytes(d, wl.num_seqs, L)
+    ws = torch.full(((nbytes + 3) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    K.paged_decode_partials(d, dq8, dqs, cache, bt, sl, L, w_group=G, workspace=ws)
+    two = K.paged_decode_merge(d, sl, L, ws)
+    alone = []
+    for i in range(wl.num_seqs):
+        Li = max(int(lens[i]), 1)
+        alone.append(K.paged_decode_int8(d, dq8[i:i + 1].contiguous(), dqs[i:i + 1].contiguous(),
+                                         cache, dev(wl.block_tables[i:i + 1]), dev(lens[i:i + 1]),
+                                         Li, w_group=G))
+    torch.cuda.synchronize()
+    one, two = one.cpu().numpy(), two.cpu().numpy()
+    alone = np.concatenate([x.cpu().numpy() for x in alone])
+    assert_bits_equal(one, alone, "batched call vs one call per sequence")
+    assert_bits_equal(two, one, "partials + merge vs the call")
+    assert not one[4].any(), "empty sequence must give zeros"
+    ocache, oq8, oqs = orc.fill(wl)
+    rows = wl.decode_query_rows()
+    ref = orc.paged_decode(oq8[rows], oqs[rows], ocache, wl.block_tables, lens,
+                           num_q_heads=wl.num_q_heads, w_group=G)
+    assert_close(one, ref, f"{wl.name} G={G}")
+
+
 def test_partials_then_merge_equal_the_call_32k(orc):
     """One 32768-token sequence: 128 partitions, merged in one 128-partition
     round (the batch-1 merge); the merge alone equals the call bit for bit."""
