@@ -1,7 +1,7 @@
 /*
  * i8kv -- paged attention over an INT8 KV cache, native to AMD MI355X (gfx950).
  *
- * C ABI of the library libi8kv.so.  Fifteen calls, on the operations defined on the pages
+ * C ABI of the library libi8kv.so.  Sixteen calls, on the operations defined on the pages
  *   [KV] "INT8 KV and INT8 MMAC attention inference optimisation on a gfx936
  *        DCU" (part 1 of the series), and
  *   [PV] "Implementing INT8 PV MMAC on a gfx936 DCU: V-scale fusion,
@@ -32,6 +32,7 @@
  *                              pages' QK comparison, [KV] 4.1)
  *   i8kv_prefix_prefill_bf16qk -- the prefill with a bf16 QK product ([KV] 4.1)
  *   i8kv_prefix_prefill_uint8w -- the prefill with UINT8 W groups ([PV] 6)
+ *   i8kv_prefix_prefill_ex  -- the prefill with options: PV variant, bf16 output
  * plus the workspace-size queries, i8kv_status_string and i8kv_abi_version.
  *
  * Conventions for every call
@@ -458,6 +459,34 @@ i8kv_status i8kv_prefix_prefill_uint8w(const i8kv_cache_desc* desc, int32_t num_
                                        int32_t w_group, float softmax_scale, void* workspace,
                                        size_t workspace_bytes, float* out,
                                        i8kv_stream_t stream);
+
+/*
+ * The prefill with options, in the serving shape of the pages' attention
+ * call ([KV] 3.2 outputs bf16):
+ *  - pv: the method's int8 W groups (I8KV_PV_INT8), the BF16-PV ablation
+ *    (I8KV_PV_BF16, w_group unused) or UINT8 W (I8KV_PV_UINT8) -- the
+ *    computations of i8kv_prefix_prefill_int8, _bf16pv and _uint8w;
+ *  - out_bf16: out [total_q, Hq, D] holds the fp32 result rounded to bf16
+ *    (nearest, ties to even; 8-byte aligned) instead of fp32.
+ * Other arguments as for i8kv_prefix_prefill_int8 (no workspace).
+ * Errors: as i8kv_prefix_prefill_int8; NULL for opts; INVALID_ARG for
+ * out_bf16 not 0/1 or a misaligned bf16 out; UNSUPPORTED for an unknown pv.
+ */
+typedef struct {
+  int32_t w_group;      /* 32 or 64 (unused by I8KV_PV_BF16) */
+  float softmax_scale;
+  int32_t pv;           /* I8KV_PV_INT8 (the method), _BF16 or _UINT8 */
+  int32_t out_bf16;     /* 0: out is fp32; 1: out is bf16 bits */
+} i8kv_prefill_opts;
+
+i8kv_status i8kv_prefix_prefill_ex(const i8kv_cache_desc* desc, const i8kv_prefill_opts* opts,
+                                   int32_t num_seqs, int32_t total_q, int32_t max_query_len,
+                                   const int8_t* q_int8, const float* q_scale,
+                                   const int32_t* query_start_loc, const int32_t* seq_lens,
+                                   const int8_t* k_cache, const int8_t* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   void* out, i8kv_stream_t stream);
 
 /*
  * The BF16-PV ablation of i8kv_prefix_prefill_int8 ([PV] 5): the same scores

@@ -25,6 +25,8 @@ fails loudly if the library has not been built -- there is no fallback.
                           cache, block_tables, ...)
     prefix_prefill_bf16qk(desc, query, query_start_loc, seq_lens, cache, block_tables, ...)
     prefix_prefill_uint8w(desc, q_int8, q_scale, query_start_loc, seq_lens, cache, ...)
+    prefix_prefill_ex(desc, q_int8, q_scale, query_start_loc, seq_lens, cache, block_tables,
+                      max_query_len, pv="int8", w_group=32, out_bf16=False, ...)
     decode_step_int8(desc, key, value, query, cache, block_tables, seq_lens, ...)
 """
 from ._binding import (  # noqa: F401
@@ -32,6 +34,7 @@ from ._binding import (  # noqa: F401
     DecodeOpts,
     I8KVError,
     PagedCache,
+    PrefillOpts,
     abi_version,
     decode_step_int8,
     kv_quantize_write,
@@ -51,6 +54,7 @@ from ._binding import (  # noqa: F401
     paged_decode_workspace_bytes,
     prefix_prefill_bf16pv,
     prefix_prefill_bf16qk,
+    prefix_prefill_ex,
     prefix_prefill_int8,
     prefix_prefill_uint8w,
     prefix_prefill_workspace_bytes,

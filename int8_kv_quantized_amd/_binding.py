@@ -36,6 +36,11 @@ class DecodeOpts(C.Structure):
                 ("queries_per_seq", C.c_int32), ("out_bf16", C.c_int32)]
 
 
+class PrefillOpts(C.Structure):
+    _fields_ = [("w_group", C.c_int32), ("softmax_scale", C.c_float), ("pv", C.c_int32),
+                ("out_bf16", C.c_int32)]
+
+
 class CacheDesc(C.Structure):
     _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("block_size", C.c_int32),
@@ -125,6 +130,9 @@ def load_library():
     lib.i8kv_prefix_prefill_uint8w.restype = C.c_int
     lib.i8kv_prefix_prefill_uint8w.argtypes = ([D, I32, I32, I32] + [P] * 9 + [I32, I32, F, P, SZ,
                                                                               P, P])
+    lib.i8kv_prefix_prefill_ex.restype = C.c_int
+    lib.i8kv_prefix_prefill_ex.argtypes = ([D, C.POINTER(PrefillOpts), I32, I32, I32] + [P] * 9
+                                           + [I32, P, P])
     lib.i8kv_prefix_prefill_int8.restype = C.c_int
     lib.i8kv_prefix_prefill_int8.argtypes = ([D, I32, I32, I32] + [P] * 9 + [I32, I32, F, P, SZ,
                                                                             P, P])
@@ -664,6 +672,44 @@ def prefix_prefill_int8(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_l
     else:
         st = lib.i8kv_prefix_prefill_int8(*common, int(w_group), *tail)
         _raise("prefix_prefill_int8", st)
+    return out
+
+
+@_allocates_on_stream
+def prefix_prefill_ex(desc: CacheDesc, q_int8, q_scale, query_start_loc, seq_lens,
+                      cache: PagedCache, block_tables, max_query_len: int, pv: str = "int8",
+                      w_group: int = 32, out_bf16: bool = False,
+                      softmax_scale: Optional[float] = None, out=None, stream=None):
+    """The prefill with options: the PV variant ("int8", "bf16", "uint8") and a
+    bf16 output (returned as torch.bfloat16); otherwise as prefix_prefill_int8."""
+    import torch
+    lib = load_library()
+    Tq = int(q_int8.shape[0])
+    S = int(seq_lens.shape[0])
+    Hq, D = desc.num_q_heads, desc.head_dim
+    _check(q_int8, "q_int8", torch.int8, (Tq, Hq, D))
+    _check(q_scale, "q_scale", torch.float32, (Tq, Hq))
+    _check(query_start_loc, "query_start_loc", torch.int32, (S + 1,))
+    _check(seq_lens, "seq_lens", torch.int32, (S,))
+    cache.check(desc)
+    _check(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError(f"block_tables: shape {tuple(block_tables.shape)}, expected ({S}, *)")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if pv not in PV_VARIANTS:
+        raise ValueError(f"pv must be one of {sorted(PV_VARIANTS)}")
+    opts = PrefillOpts(int(w_group), float(softmax_scale), PV_VARIANTS[pv], 1 if out_bf16 else 0)
+    dt = torch.bfloat16 if out_bf16 else torch.float32
+    if out is None:
+        out = torch.empty((Tq, Hq, D), dtype=dt, device=q_int8.device)
+    _check(out, "out", dt, (Tq, Hq, D))
+    st = lib.i8kv_prefix_prefill_ex(
+        C.byref(desc), C.byref(opts), S, Tq, int(max_query_len), _ptr(q_int8), _ptr(q_scale),
+        _ptr(query_start_loc), _ptr(seq_lens), _ptr(cache.k_cache), _ptr(cache.v_cache),
+        _ptr(cache.k_scale), _ptr(cache.v_scale), _ptr(block_tables), int(block_tables.shape[1]),
+        _ptr(out), _stream(stream))
+    _raise("prefix_prefill_ex", st)
     return out
 
 

@@ -117,13 +117,14 @@ i8kv_status run_prefill(const i8kv_cache_desc* desc, int32_t num_seqs,
                                      int32_t w_group, float softmax_scale, void* workspace,
                                      size_t workspace_bytes, float* out,
                                      i8kv_stream_t stream, bool pv_bf16,
-                                     const uint16_t* q_bf16 = nullptr, bool w_uint8 = false) {
+                                     const uint16_t* q_bf16 = nullptr, bool w_uint8 = false,
+                                     uint16_t* out16 = nullptr) {
   (void)workspace;
   (void)workspace_bytes;
   i8kv_status st = check_desc(desc);
   if (st != I8KV_OK) return st;
   if ((!q_bf16 && (!q_int8 || !q_scale)) || !query_start_loc || !seq_lens || !k_cache ||
-      !v_cache || !k_scale || !v_scale || !block_tables || !out)
+      !v_cache || !k_scale || !v_scale || !block_tables || (!out && !out16))
     return I8KV_ERR_NULL;
   if (num_seqs < 0 || total_q < 0 || max_query_len < 0 || max_blocks_per_seq <= 0)
     return I8KV_ERR_INVALID_ARG;
@@ -134,6 +135,7 @@ i8kv_status run_prefill(const i8kv_cache_desc* desc, int32_t num_seqs,
   if ((q_bf16 ? !aligned16(q_bf16) : !aligned16(q_int8)) || !aligned16(k_cache) ||
       !aligned16(v_cache))
     return I8KV_ERR_INVALID_ARG;
+  if (out16 && (reinterpret_cast<uintptr_t>(out16) & 7)) return I8KV_ERR_INVALID_ARG;
   if (num_seqs == 0 || total_q == 0) return I8KV_OK;
   PrefillArgs a{};
   a.num_seqs = num_seqs;
@@ -159,7 +161,8 @@ i8kv_status run_prefill(const i8kv_cache_desc* desc, int32_t num_seqs,
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.block_tables = block_tables;
-  a.out = out;
+  a.out = out16 ? nullptr : out;
+  a.out16 = out16;
   return from_hip(launch_clean(launch_prefix_prefill, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -554,6 +557,27 @@ i8kv_status i8kv_prefix_prefill_uint8w(const i8kv_cache_desc* desc, int32_t num_
                      seq_lens, k_cache, v_cache, k_scale, v_scale, block_tables,
                      max_blocks_per_seq, w_group, softmax_scale, workspace, workspace_bytes, out,
                      stream, false, nullptr, /*w_uint8=*/true);
+}
+
+i8kv_status i8kv_prefix_prefill_ex(const i8kv_cache_desc* desc, const i8kv_prefill_opts* opts,
+                                   int32_t num_seqs, int32_t total_q, int32_t max_query_len,
+                                   const int8_t* q_int8, const float* q_scale,
+                                   const int32_t* query_start_loc, const int32_t* seq_lens,
+                                   const int8_t* k_cache, const int8_t* v_cache,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   void* out, i8kv_stream_t stream) {
+  if (!opts) return I8KV_ERR_NULL;
+  if (opts->pv != I8KV_PV_INT8 && opts->pv != I8KV_PV_BF16 && opts->pv != I8KV_PV_UINT8)
+    return I8KV_ERR_UNSUPPORTED;
+  if (opts->out_bf16 != 0 && opts->out_bf16 != 1) return I8KV_ERR_INVALID_ARG;
+  const bool bf16 = opts->pv == I8KV_PV_BF16;
+  return run_prefill(desc, num_seqs, total_q, max_query_len, q_int8, q_scale, query_start_loc,
+                     seq_lens, k_cache, v_cache, k_scale, v_scale, block_tables,
+                     max_blocks_per_seq, bf16 ? 64 : opts->w_group, opts->softmax_scale, nullptr,
+                     0, opts->out_bf16 ? nullptr : static_cast<float*>(out), stream, bf16,
+                     nullptr, opts->pv == I8KV_PV_UINT8,
+                     opts->out_bf16 ? static_cast<uint16_t*>(out) : nullptr);
 }
 
 i8kv_status i8kv_prefix_prefill_bf16pv(const i8kv_cache_desc* desc, int32_t num_seqs,

@@ -100,6 +100,7 @@ struct PrefillArgs {
   const float* v_scale;
   const int32_t* block_tables;
   float* out;
+  uint16_t* out16;  // bf16 output instead of out (nearest, ties to even)
 };
 
 hipError_t launch_prefix_prefill(const PrefillArgs& a, hipStream_t stream);

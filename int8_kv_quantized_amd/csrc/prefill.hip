@@ -572,6 +572,15 @@ __global__ __launch_bounds__(PrefillShape<QB>::NW * kWave) void prefix_prefill_k
   const float l_row = row_sum4(lsum);
   if (!row_ok) return;
   const float inv = 1.0f / l_row;
+  if (a.out16) {  // the same fp32 values, rounded to bf16 (nearest, ties to even)
+    uint16_t* dst = a.out16 + qrow * D + 4 * lg;
+#pragma unroll
+    for (int n = 0; n < NN; ++n)
+      *reinterpret_cast<uint2*>(dst + 16 * n) =
+          make_uint2(bf16_rne_bits((O[n][0] - rc) * inv) | (bf16_rne_bits((O[n][1] - rc) * inv) << 16),
+                     bf16_rne_bits((O[n][2] - rc) * inv) | (bf16_rne_bits((O[n][3] - rc) * inv) << 16));
+    return;
+  }
   float* dst = a.out + qrow * D + 4 * lg;
 #pragma unroll
   for (int n = 0; n < NN; ++n)

@@ -30,7 +30,8 @@ def test_header_declares_the_operations():
                "i8kv_prefix_prefill_int8", "i8kv_prefix_prefill_bf16pv", "i8kv_decode_step_int8",
                "i8kv_paged_decode_bf16qk", "i8kv_prefix_prefill_bf16qk",
                "i8kv_paged_decode_partials", "i8kv_paged_decode_merge",
-               "i8kv_prefix_prefill_uint8w", "i8kv_paged_decode_int8_noalloc"):
+               "i8kv_prefix_prefill_uint8w", "i8kv_paged_decode_int8_noalloc",
+               "i8kv_prefix_prefill_ex"):
         assert op in names
 
 
@@ -323,6 +324,33 @@ def test_decode_step_descriptor_checked_first():
 
 
 # --- prefill ------------------------------------------------------------------
+def prefill_ex(d, opts_kw=None, S=1, Tq=8, max_q=8, q8=FAKE, out=FAKE, no_opts=False):
+    P = lambda x: None if x is None else C.c_void_p(x)
+    o = dict(w_group=32, softmax_scale=0.0625, pv=0, out_bf16=0)
+    o.update(opts_kw or {})
+    opts = K.PrefillOpts(**o)
+    return _lib().i8kv_prefix_prefill_ex(
+        None if d is None else C.byref(d), None if no_opts else C.byref(opts), S, Tq, max_q,
+        P(q8), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 32, P(out),
+        None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(no_opts=True), NULL), (dict(q8=None), NULL), (dict(out=None), NULL),
+    (dict(opts_kw=dict(pv=3)), UNSUPPORTED), (dict(opts_kw=dict(out_bf16=2)), INVALID),
+    (dict(opts_kw=dict(w_group=48)), UNSUPPORTED),
+    (dict(opts_kw=dict(out_bf16=1), out=FAKE + 4), INVALID),   # bf16 out: 8-byte aligned
+    (dict(opts_kw=dict(out_bf16=1), out=FAKE + 8, S=0), OK),
+    (dict(S=0, opts_kw=dict(pv=1, w_group=7)), OK),           # w_group unused by the bf16 PV
+    (dict(S=0, opts_kw=dict(pv=2, out_bf16=1)), OK),
+    (dict(S=-1), INVALID),
+])
+def test_prefill_ex_validation(kw, expect):
+    assert prefill_ex(desc(), **kw) == expect
+    assert prefill_ex(None) == NULL
+
+
+
 @pytest.mark.parametrize("kw,expect", [
     (dict(S=-1), INVALID), (dict(Tq=-1), INVALID), (dict(max_q=9), INVALID),
     (dict(G=16), UNSUPPORTED), (dict(scale=float("inf")), INVALID),
