@@ -530,8 +530,10 @@ i8kv_status i8kv_prefix_prefill_bf16qk(const i8kv_cache_desc* desc, int32_t num_
                                        size_t workspace_bytes, float* out,
                                        i8kv_stream_t stream);
 
-/* Human-readable name of a status code (static string). */
-const char* i8kv_status_string(i8kv_status status);
+/* Human-readable name of a status code (static string); any other value
+ * gives "unknown status".  Takes the code as an int32_t so that a value no
+ * i8kv_status names is still a valid argument. */
+const char* i8kv_status_string(int32_t status);
 
 /* I8KV_ABI_VERSION of the loaded library. */
 int32_t i8kv_abi_version(void);

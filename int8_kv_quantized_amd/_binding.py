@@ -85,7 +85,7 @@ def load_library():
     lib.i8kv_abi_version.restype = I32
     lib.i8kv_abi_version.argtypes = []
     lib.i8kv_status_string.restype = C.c_char_p
-    lib.i8kv_status_string.argtypes = [C.c_int]
+    lib.i8kv_status_string.argtypes = [C.c_int32]
     lib.i8kv_kv_quantize_write.restype = C.c_int
     lib.i8kv_kv_quantize_write.argtypes = [D, I32] + [P] * 10 + [P]
     lib.i8kv_kv_quantize_write_rope.restype = C.c_int

@@ -172,7 +172,7 @@ extern "C" {
 
 int32_t i8kv_abi_version(void) { return I8KV_ABI_VERSION; }
 
-const char* i8kv_status_string(i8kv_status s) {
+const char* i8kv_status_string(int32_t s) {
   switch (s) {
     case I8KV_OK: return "ok";
     case I8KV_ERR_NULL: return "null pointer argument";

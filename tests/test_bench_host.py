@@ -42,17 +42,33 @@ def _tree_with(tmp_path, records, edit_source=False):
 
 
 def test_traffic_is_the_committed_per_launch_bytes_of_the_partition_kernel():
+    """The committed record's bytes while the hashed sources are those it was
+    taken on, null otherwise (a stale count is never reported)."""
+    import hashlib
     recs = json.loads((ROOT / "profiles" / "hbm_traffic.json").read_text())
     rec = [r for r in recs if r["workload"] == "decode_L16384_outlierV_G32" and r["w_group"] == 32][0]
-    assert bench.counted_traffic("decode_L16384_outlierV_G32", 32) == rec["hbm_bytes_per_launch"]
+    h = hashlib.sha256()
+    for src in bench.DECODE_SOURCES:
+        h.update((ROOT / src).read_bytes())
+    want = rec["hbm_bytes_per_launch"] if h.hexdigest() == rec["kernel_sources_sha256"] else None
+    assert bench.counted_traffic("decode_L16384_outlierV_G32", 32) == want
     # the partition kernel moves at least the algorithmic K/V + scale bytes
     assert rec["hbm_bytes_per_launch"] >= 34078720
     assert bench.counted_traffic("decode_L16384_outlierV_G32", 64) is None
     assert bench.counted_traffic("decode_L512", 32) is None
 
 
+def _rehashed(recs):
+    """The committed records, keyed to the current decode sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for src in bench.DECODE_SOURCES:
+        h.update((ROOT / src).read_bytes())
+    return [dict(r, kernel_sources_sha256=h.hexdigest()) for r in recs]
+
+
 def test_traffic_is_null_once_a_decode_source_changes(tmp_path, monkeypatch):
-    recs = json.loads((ROOT / "profiles" / "hbm_traffic.json").read_text())
+    recs = _rehashed(json.loads((ROOT / "profiles" / "hbm_traffic.json").read_text()))
     _tree_with(tmp_path, recs)
     monkeypatch.setattr(bench, "ROOT", tmp_path)
     assert bench.counted_traffic("decode_L16384_outlierV_G32", 32) is not None
@@ -62,7 +78,7 @@ def test_traffic_is_null_once_a_decode_source_changes(tmp_path, monkeypatch):
 
 
 def test_traffic_needs_a_per_launch_record(tmp_path, monkeypatch):
-    recs = json.loads((ROOT / "profiles" / "hbm_traffic.json").read_text())
+    recs = _rehashed(json.loads((ROOT / "profiles" / "hbm_traffic.json").read_text()))
     for r in recs:
         r.pop("hbm_bytes_per_launch")   # a call-level record is not a launch's traffic
     _tree_with(tmp_path, recs)
