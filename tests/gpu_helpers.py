@@ -107,3 +107,57 @@ def row_tile_ends(total_rows, tile=32):
     """First and last query row of every ``tile``-row tile of a chunk."""
     starts = np.arange(0, total_rows, tile)
     return np.unique(np.concatenate([starts, np.minimum(starts + tile - 1, total_rows - 1)]))
+
+
+def prefill_tie_allowance(orc, q8, qs, qsl, seq_lens, cache, block_tables, row, head, G,
+                          flags=0, delta=1e-4):
+    """Per output dim of one prefill (row, head): the most the kernel may
+    differ from the oracle because of W codes that sit at a rounding tie.
+
+    A code is decided by rounding W / sW; where that quotient lies within
+    `delta` of a half-integer, the kernel's own fp32 W (base-2 exponential,
+    its reference max, a reciprocal, ties to even) may fall on the other side
+    of the tie than the oracle's IEEE quotient, and either code is a correct
+    decision.  Changing one such code by one unit moves the output by
+    sW |Vq[d]| / l; the allowance is the sum over the row's tie codes (zero
+    for a row without one).  Codes: the oracle's trace of the row."""
+    t = orc.prefill_row(q8, qs, qsl, seq_lens, cache, block_tables, row, head, w_group=G,
+                        flags=flags)
+    nk = t["nk"]
+    keys = np.arange(nk)
+    b = int(np.searchsorted(qsl, row, side="right") - 1)
+    Hq = q8.shape[1]
+    Hkv = cache["k_cache"].shape[1]
+    kv = head // (Hq // Hkv)
+    page = block_tables[b, keys // 16]
+    off = keys % 16
+    sv = cache["v_scale"][page, off, kv]
+    vq = cache["v_cache"][page, kv, :, off].astype(np.float64)       # [nk, D]
+    W = (t["ptil"] * sv).astype(np.float32)
+    sW = t["sW"][keys // G].astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(sW > 0, W / np.where(sW > 0, sW, 1), 0).astype(np.float64)
+    tie = (sW > 0) & (np.abs(q - np.floor(q) - 0.5) <= delta)
+    return (sW[tie, None].astype(np.float64) * np.abs(vq[tie])).sum(axis=0) / float(t["l"][0])
+
+
+def assert_close_prefill(got, ref, rows, tie_fn, what, max_abs=1e-3, mean_abs=1e-4):
+    """assert_close for prefill rows, except that an element of a (row, head)
+    whose max-abs exceeds max_abs may differ by max_abs plus that row's tie
+    allowance (tie_fn(row, head) -> per-dim allowance; prefill_tie_allowance).
+    mean-abs is checked over everything, unchanged."""
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    mx, mn = float(err.max()), float(err.mean())
+    say(f"    {what}: max-abs {mx:.3e}  mean-abs {mn:.3e}")
+    assert mn <= mean_abs, f"{what}: mean-abs {mn:.3e}"
+    over = np.argwhere(err.max(axis=2) > max_abs)
+    for i, h in over:
+        a = tie_fn(int(rows[i]), int(h))
+        assert a.max() > 0, f"{what}: row {rows[i]} head {h} max-abs {err[i, h].max():.3e}, no tie code"
+        assert np.all(err[i, h] <= max_abs + a), (
+            f"{what}: row {rows[i]} head {h} max-abs {err[i, h].max():.3e} beyond its tie codes")
+    if over.size:
+        say(f"    {len(over)} (row, head) pairs past {max_abs:g}, each explained by W codes at a "
+            f"rounding tie")
+    return mx, mn

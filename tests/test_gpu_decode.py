@@ -122,6 +122,17 @@ def test_decode_cfg5_mha(orc, G):
     run_decode(W.cfg5_mha_producer_decode(G), orc, G)
 
 
+def test_decode_many_sequences(orc):
+    """700 sequences of seeded lengths 1 .. 700 (one to three partitions):
+    700 workgroup rows in the grid of both kernels, every length class."""
+    rng = np.random.default_rng(71)
+    lens = rng.integers(1, 701, 700)
+    wl = W.make_workload("many_seqs", seq_lens=tuple(int(x) for x in lens),
+                         new_tokens=[1] * lens.size, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                         seed=71)
+    run_decode(wl, orc, 32, report=False)
+
+
 def test_decode_long_sequences_many_merge_rounds(orc):
     """150001 and 70000 tokens: 586 and 274 partitions, so the merge runs
     ten and five rounds of 64 partitions, with ragged last partitions."""

@@ -4,14 +4,19 @@ Small ragged cases compare every output.  The full 2048-over-16384 chunk is
 compared on every one of its 2048 query rows and 24 heads (the oracle runs on
 a host thread pool); the error against unquantized fp64 attention is reported
 on the first and last row of every 32-row tile.  Tolerance: max-abs 1e-3,
-mean-abs 1e-4.
+mean-abs 1e-4, except that a W code whose quotient W / sW lies within 1e-4 of
+a rounding tie may be decided either way (one code unit of that key's
+contribution, sW |Vq| / l, on top of 1e-3 for that row; see
+gpu_helpers.prefill_tie_allowance) -- with few keys per row (small l) one
+such code alone can move an output past 1e-3.
 """
 import numpy as np
 import pytest
 
 import workloads as W
-from gpu_helpers import (assert_bits_equal, assert_close, cache_to_np, dev, gpu_fill,
-                         oracle_rows, report_fp64, row_tile_ends, say)
+from gpu_helpers import (assert_bits_equal, assert_close, assert_close_prefill, cache_to_np, dev,
+                         gpu_fill, oracle_rows, prefill_tie_allowance, report_fp64,
+                         row_tile_ends, say)
 from refmath import prefill_reference_fp64
 
 pytestmark = pytest.mark.gpu
@@ -39,7 +44,9 @@ def run_prefill(wl, orc, G, rows=None, fp64_rows=None):
                                                       wl.block_tables, w_group=G, **kw),
                       r, np.zeros_like(out))
     say(f"    compared {r.size} query rows x {wl.num_q_heads} heads")
-    assert_close(out[r], ref[r], f"{wl.name} G={G}")
+    tie = lambda row, head: prefill_tie_allowance(orc, oq8, oqs, qsl, wl.seq_lens, ocache,
+                                                  wl.block_tables, row, head, G)
+    assert_close_prefill(out[r], ref[r], r, tie, f"{wl.name} G={G}")
     r64 = r if fp64_rows is None else np.asarray(fp64_rows, np.int32)
     ref64 = prefill_reference_fp64(wl, rows=r64)
     report_fp64(out[r64], ref64[r64], f"{wl.name} G={G} ({r64.size} rows)")
@@ -55,6 +62,20 @@ SMALL = [
     dict(name="d256_g16", seq_lens=(200,), new_tokens=(65,), num_q_heads=16, num_kv_heads=1,
          head_dim=256),
 ]
+
+
+def test_prefill_many_sequences(orc):
+    """200 sequences: seeded histories of 0 .. 400 tokens and chunks of 1 .. 24
+    queries (200 workgroup planes in the grid; short and empty histories,
+    chunks shorter than a row tile)."""
+    rng = np.random.default_rng(72)
+    chunks = rng.integers(1, 25, 200)
+    hist = rng.integers(0, 401, 200)
+    wl = W.make_workload("many_seqs_prefill", seed=72, kind="prefill",
+                         seq_lens=tuple(int(h + c) for h, c in zip(hist, chunks)),
+                         new_tokens=tuple(int(c) for c in chunks), num_q_heads=6,
+                         num_kv_heads=2, head_dim=128, w_group=32)
+    run_prefill(wl, orc, 32)
 
 
 @pytest.mark.parametrize("G", [32, 64])
