@@ -345,6 +345,29 @@ __device__ __forceinline__ void rope_wave_vector(float (&x)[D / kWave], int lane
   }
 }
 
+// The same rotation over the whole head (R = D), with the token's table row
+// already in registers as loaded by lanes in order: lane l holds row entries
+// D/64 l .. D/64 l + D/64 - 1, i.e. the cosines of lanes 0-31 and the sines
+// of lanes 32-63 for the same pair index.  Element i of lane l pairs with
+// element i of lane l ^ 32, so one v_permlane32_swap per register gives each
+// lane both its partner's element and the cosine and sine of its pair.
+template <int D>
+__device__ __forceinline__ void rope_wave_vector_full(float (&x)[D / kWave], int lane,
+                                                      const float (&cs)[D / kWave]) {
+#pragma clang fp contract(off)
+  constexpr int EPL = D / kWave;
+  const bool lower = lane < 32;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    uint32_t lo, hi, c, sn;
+    swap32(f_bits(x[i]), lo, hi);      // lo: element of lane l % 32, hi: of lane l % 32 + 32
+    swap32(f_bits(cs[i]), c, sn);      // c: cosine, sn: sine of the pair
+    const float p = bits_f(lower ? hi : lo);
+    const float a = x[i] * bits_f(c), b = p * bits_f(sn);
+    x[i] = lower ? a - b : a + b;
+  }
+}
+
 // The lane's D/64 bf16 elements of a D-vector (see quantize_wave_vector).
 // NT: non-temporal loads (read-once inputs of the producer: the 2242- and
 // 4096-token chunks measured 5-8% faster); the fused decode step reads its one

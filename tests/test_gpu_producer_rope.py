@@ -81,6 +81,40 @@ def test_rope_producer_small(orc, kw, table):
     _compare(orc, wl, pos, cs)
 
 
+CHUNK = [
+    dict(name="chunk_d256_r256", num_q_heads=24, num_kv_heads=4, head_dim=256, R=256),
+    dict(name="chunk_d256_r64", num_q_heads=24, num_kv_heads=4, head_dim=256, R=64),
+    dict(name="chunk_d128_r128", num_q_heads=8, num_kv_heads=2, head_dim=128, R=128),
+    dict(name="chunk_d128_r4", num_q_heads=6, num_kv_heads=2, head_dim=128, R=4),
+    dict(name="chunk_d64_r64", num_q_heads=4, num_kv_heads=4, head_dim=64, R=64),
+    dict(name="chunk_d64_r2", num_q_heads=4, num_kv_heads=2, head_dim=64, R=2),
+]
+
+
+@pytest.mark.parametrize("kw", CHUNK, ids=lambda k: k["name"])
+@pytest.mark.parametrize("table", ["standard", "random"])
+def test_rope_producer_chunks(orc, kw, table):
+    """Calls of 128 tokens or more (the 16-token-per-wave kernel, with the
+    table rows prefetched when the rotation covers the whole head): both
+    calls of the fill are chunks (221 history tokens, 203 new ones with
+    their queries), 16-token groups straddle sequences and pages, the last
+    group is ragged, and some slots are skipped."""
+    kw = dict(kw)
+    name, R = kw.pop("name"), kw.pop("R")
+    wl = W.make_workload(name, seq_lens=(290, 134), new_tokens=(141, 62), seed=57, **kw)
+    wl.slot_mapping[7::37] = -1
+    rng = np.random.default_rng(58)
+    if table == "standard":
+        cs = W.rope_cos_sin(int(wl.seq_lens.max()), R)
+        pos = wl.token_pos
+    else:
+        cs = W.random_cos_sin(rng, 301, R)
+        pos = rng.integers(0, 301, wl.num_tokens).astype(np.int32)
+    hist, qi = split_tokens(wl)
+    assert hist.size >= 128 and qi.size >= 128
+    _compare(orc, wl, pos, cs)
+
+
 def test_rope_identity_table_matches_plain_producer(orc):
     """cos 1 / sin 0 everywhere: the same bits as the producer without RoPE."""
     from gpu_helpers import gpu_fill
