@@ -99,7 +99,9 @@ constexpr int decode_min_waves() {
 // QB: the BF16-QK ablation -- the bf16 queries (not quantized) against the
 // int8 K codes taken exactly as bf16, v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation, score = (dot * sK) * softmax_scale; the rest is unchanged.
-template <int D, int G, bool FUSED, int PVM, bool MQ, bool QB>
+// NTP: the partials go out with non-temporal stores (chosen at launch for
+// grids of several rounds).
+template <int D, int G, bool FUSED, int PVM, bool MQ, bool QB, bool NTP = false>
 __global__ __launch_bounds__(DecodeShape<D>::NW * kWave, (decode_min_waves<D, G, PVM, MQ, QB>())) void
 paged_decode_partition_kernel(
     DecodeArgs a) {
@@ -567,13 +569,20 @@ paged_decode_partition_kernel(
           if (a.out16) a.out16[obase[r] + dim] = (uint16_t)bf16_rne_bits(o[c][r]);
           else a.out[obase[r] + dim] = o[c][r];
         }
+        else if constexpr (NTP) __builtin_nontemporal_store(o[c][r], a.part_o + (node + h) * D + dim);
         else a.part_o[(node + h) * D + dim] = o[c][r];
       }
     }
   }
   if (!direct && tid < rows) {
-    a.part_ml[(node + tid) * 2] = s_M[tid];
-    a.part_ml[(node + tid) * 2 + 1] = s_L[tid];
+    float* ml = a.part_ml + (node + tid) * 2;
+    if constexpr (NTP) {
+      __builtin_nontemporal_store(s_M[tid], ml);
+      __builtin_nontemporal_store(s_L[tid], ml + 1);
+    } else {
+      ml[0] = s_M[tid];
+      ml[1] = s_L[tid];
+    }
   }
 }
 
@@ -706,8 +715,21 @@ void launch_merge(const DecodeArgs& a, dim3 mgrid, hipStream_t stream) {
     hipLaunchKernelGGL((paged_decode_merge_kernel<D, 8>), mgrid, dim3(kWave), 0, stream, a);
 }
 
+// Grids of more workgroups than the chip has CUs (256) run in several
+// rounds; when each workgroup also writes kilobytes of partials, the plain
+// and fused int8 kernels store them with the non-temporal hint (A/B in one
+// process: batch 16 at L ~ U[1K, 32K], 6 KB per workgroup, partition kernel
+// 123.3 -> 119.2 us; 32K call 19.22 -> 18.99 us).  A grid of one round keeps
+// ordinary stores (16K: 9.63 against 9.84 us with the hint), and so do small
+// partials (the MHA batch, 512 B per workgroup: 100.5 against 101.3 us).
+constexpr int64_t kNtPartialsMinGroups = 257;
+constexpr int64_t kNtPartialsMinBytes = 4096;
+
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
+  const bool ntp =
+      (int64_t)a.max_parts * a.num_kv_heads * a.num_seqs >= kNtPartialsMinGroups &&
+      (int64_t)a.group * a.nq * a.head_dim * (int64_t)sizeof(float) >= kNtPartialsMinBytes;
   dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
   dim3 mgrid((unsigned)(a.num_q_heads * a.nq), (unsigned)a.num_seqs, (unsigned)(a.head_dim / 32));
 #define I8KV_DECODE_CASE(DD, GG)                                                                 \
@@ -718,7 +740,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
       launch_merge<DD>(a, mgrid, stream);                                                        \
       return hipGetLastError();                                                                  \
     }                                                                                            \
-    if (a.new_key)                                                                               \
+    if (a.new_key && ntp)                                                                        \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8, false, false, true>), \
+                         grid, blk, 0, stream, a);                                               \
+    else if (a.new_key)                                                                          \
       hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8, false, false>),   \
                          grid, blk, 0, stream, a);                                               \
     else if (a.q_bf16)                                                                           \
@@ -738,6 +763,9 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
                          grid, blk, 0, stream, a);                                               \
     else if (mq)                                                                                 \
       hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, true, false>),   \
+                         grid, blk, 0, stream, a);                                               \
+    else if (ntp)                                                                                \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false, false, true>), \
                          grid, blk, 0, stream, a);                                               \
     else                                                                                         \
       hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false, false>),  \

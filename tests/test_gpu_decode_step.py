@@ -77,6 +77,10 @@ CASES = [
     dict(name="step_d64_g16", seq_lens=(40, 300, 1), num_q_heads=16, num_kv_heads=1, head_dim=64),
     dict(name="step_d256_g6", seq_lens=(600, 4097), num_q_heads=24, num_kv_heads=4, head_dim=256),
     dict(name="step_mha_d128", seq_lens=(1000, 16), num_q_heads=8, num_kv_heads=8, head_dim=128),
+    # 122 partitions x 4 KV heads x 5 sequences: a grid of several rounds with
+    # 6 KB of partials per workgroup (the non-temporal-store instantiations)
+    dict(name="step_d256_g6_rounds", seq_lens=(20000, 1, 9000, 31000, 257), num_q_heads=24,
+         num_kv_heads=4, head_dim=256),
 ]
 
 
