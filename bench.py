@@ -427,21 +427,7 @@ def time_producer_chunk(tokens, steps=50, min_rotation_mb=512.0):
 
     res = {}
     for name, fn, extra_b in (("plain", plain, 0), ("rope", rope, 4 + 4 * R)):
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(steps):
-                fn(i)
-        g.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / steps
+        us = _graph_us(fn, steps, reps=5)
         b = T * (per_tok + extra_b)
         res[f"{name}_us"] = round(us, 3)
         res[f"{name}_gbs"] = round(b / (us * 1e-6) / 1e9, 1)
@@ -573,21 +559,7 @@ def time_multi_query(G=32, steps=20, min_rotation_mb=512.0):
     for name, fn in (("multi_query_us", lambda i: multi(i, o32)),
                      ("multi_query_bf16_out_us", lambda i: multi(i, o16)),
                      ("separate_calls_us", separate)):
-        for i in range(2):
-            fn(i)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(steps):
-                fn(i)
-        g.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        res[name] = round(1e3 * e0.elapsed_time(e1) / steps, 3)
+        res[name] = round(_graph_us(fn, steps, reps=5), 3)
     eff = wl.effective_kv_bytes()
     res["multi_query_gbs"] = round(eff / (res["multi_query_us"] * 1e-6) / 1e9, 1)
     res["speedup_vs_separate"] = round(res["separate_calls_us"] / res["multi_query_us"], 3)
