@@ -112,7 +112,9 @@ def row_tile_ends(total_rows, tile=32):
 def prefill_tie_allowance(orc, q8, qs, qsl, seq_lens, cache, block_tables, row, head, G,
                           flags=0, delta=1e-4):
     """Per output dim of one prefill (row, head): the most the kernel may
-    differ from the oracle because of W codes that sit at a rounding tie.
+    differ from the oracle because of W codes that sit at a rounding tie
+    ("Implementing INT8 PV MMAC on a gfx936 DCU", section 1: Wq = round(W / sW),
+    with W = p~ sV of section 2.1).
 
     A code is decided by rounding W / sW; where that quotient lies within
     `delta` of a half-integer, the kernel's own fp32 W (base-2 exponential,
