@@ -568,23 +568,27 @@ def time_multi_query(G=32, steps=20, min_rotation_mb=512.0):
 
 DECODE_SOURCES = ["int8_kv_quantized_amd/csrc/decode.hip", "int8_kv_quantized_amd/csrc/kernels.hpp",
                   "int8_kv_quantized_amd/csrc/device_common.hpp"]
+PREFILL_SOURCES = ["int8_kv_quantized_amd/csrc/prefill.hip", "int8_kv_quantized_amd/csrc/kernels.hpp",
+                   "int8_kv_quantized_amd/csrc/device_common.hpp"]
 
 
-def counted_traffic(workload, G):
-    """HBM bytes per launch of the decode's partition kernel from the committed
-    FETCH_SIZE / WRITE_SIZE counters (profiles/hbm_traffic.json), or None when
-    no record matches the workload or the decode kernel sources changed since
-    they were taken."""
+def counted_traffic(workload, G, sources=None):
+    """HBM bytes per launch of a kernel from the committed FETCH_SIZE /
+    WRITE_SIZE counters (profiles/hbm_traffic.json): the decode's partition
+    kernel (sources DECODE_SOURCES, the default) or the prefill kernel
+    (PREFILL_SOURCES).  None when no record matches the workload, or when the
+    kernel's sources changed since the counters were taken."""
     import hashlib
+    sources = DECODE_SOURCES if sources is None else sources
     path = ROOT / "profiles" / "hbm_traffic.json"
     if not path.exists():
         return None
     h = hashlib.sha256()
-    for s in DECODE_SOURCES:
+    for s in sources:
         h.update((ROOT / s).read_bytes())
     for rec in json.loads(path.read_text()):
         if (rec.get("workload") == workload and rec.get("w_group") == G
-                and rec.get("kernel_sources") == DECODE_SOURCES
+                and rec.get("kernel_sources") == sources
                 and rec.get("kernel_sources_sha256") == h.hexdigest()
                 and "hbm_bytes_per_launch" in rec):
             return int(rec["hbm_bytes_per_launch"])
@@ -830,8 +834,15 @@ def main():
             pf = time_prefill(args.prefill_reps, G, graph=not args.no_graph,
                               min_rotation_mb=args.min_rotation_mb, keep_rows=rows)
             pouts[G] = pf["rows_out"]
-            precs[f"G{G}"] = dict(us=round(pf["us"], 2), int8_tops=round(pf["tops"], 2),
-                                  frac_int8_peak=round(pf["tops"] / INT8_PEAK_TOPS, 4))
+            precs[f"G{G}"] = dict(
+                us=round(pf["us"], 2), int8_tops=round(pf["tops"], 2),
+                frac_int8_peak=round(pf["tops"] / INT8_PEAK_TOPS, 4),
+                # the prefill kernel is the call's only launch
+                roofline={"bound": "mfma", "achieved": round(pf["tops"], 2),
+                          "peak": INT8_PEAK_TOPS, "unit": "int8 TOP/s",
+                          "frac": round(pf["tops"] / INT8_PEAK_TOPS, 4),
+                          "traffic": counted_traffic(pf["workload"], G, PREFILL_SOURCES),
+                          "kernel": f"prefix_prefill_kernel<256,{G}>"})
             log(f"prefill {pf['workload']} G={G}: {pf['us']:.1f} us, {pf['tops']:.1f} int8 TOPS "
                 f"({100 * pf['tops'] / INT8_PEAK_TOPS:.1f}% of peak)")
             if G == 32:
