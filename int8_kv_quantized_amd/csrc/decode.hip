@@ -218,7 +218,12 @@ paged_decode_partition_kernel(
   float sk[PPW];
   float sv_ld;
   v4i kb[PPW][NC];
+  int pidv_raw[4];  // fused step: the table entries as read (the newest token's page is one)
   auto second_round_trip = [&]() {
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) pidv_raw[g] = pidv[g];
+    }
 #pragma unroll
     for (int j = 0; j < PPW; ++j) pidk[j] = clamp_page(pidk[j]);
 #pragma unroll
@@ -292,7 +297,12 @@ paged_decode_partition_kernel(
           // the producer's cache write of the newest token (slot from the table)
           if (lane == 0) s_nsc[it - grp] = sc;
           const int pos = L - 1;
-          const int blk = bt_row[min(pos / kBlockSize, a.max_blocks_per_seq - 1)];
+          // page j of this partition's 16 was read in the first round trip by
+          // the lanes of group j % 4, as entry j / 4 (no second table read,
+          // whose wait would have included every load in flight)
+          const int j = pos / kBlockSize - 16 * p;
+          const int pv = j < 4 ? pidv_raw[0] : j < 8 ? pidv_raw[1] : j < 12 ? pidv_raw[2] : pidv_raw[3];
+          const int blk = __builtin_amdgcn_readlane(pv, 16 * (j & 3));
           if (blk >= 0 && blk < a.num_blocks) {
             const int off = pos % kBlockSize;
             if (it == grp) store_k_token<D>(a.k_cache_w, blk, kv, Hkv, off, lane, codes);
