@@ -99,9 +99,14 @@ constexpr int decode_min_waves() {
 // QB: the BF16-QK ablation -- the bf16 queries (not quantized) against the
 // int8 K codes taken exactly as bf16, v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation, score = (dot * sK) * softmax_scale; the rest is unchanged.
-// NTP: the partials go out with non-temporal stores (chosen at launch for
-// grids of several rounds).
-template <int D, int G, bool FUSED, int PVM, bool MQ, bool QB, bool NTP = false>
+// Grid modes, chosen at launch: one round of workgroups (at most one per CU);
+// several rounds -- the length is checked before any vector load, so a
+// workgroup past its sequence leaves without waiting for loads it would not
+// use; several rounds with kilobytes of partials per workgroup -- also the
+// partials go out with non-temporal stores.
+enum : int { kOneRound = 0, kRounds = 1, kRoundsNt = 2 };
+
+template <int D, int G, bool FUSED, int PVM, bool MQ, bool QB, int MODE = kOneRound>
 __global__ __launch_bounds__(DecodeShape<D>::NW * kWave, (decode_min_waves<D, G, PVM, MQ, QB>())) void
 paged_decode_partition_kernel(
     DecodeArgs a) {
@@ -146,6 +151,16 @@ paged_decode_partition_kernel(
   // pages this thread reads, the queries and their scales.  None of them
   // depends on another, so they are all in flight together.
   const int L_raw = a.seq_lens[s];
+  if constexpr (MODE != kOneRound) {
+    // In a grid of several rounds many workgroups lie past their sequence
+    // (the grid is sized by max_seq_len): they leave on the length alone,
+    // before issuing the loads below -- batch 16 at L ~ U[1K, 32K], 45% of
+    // the 8000 workgroups: partition kernel 119.1 -> 113.7 us; one long
+    // sequence (32K, all workgroups live) unchanged.  Partition 0 of an empty
+    // sequence stays (it writes the zeros, or the fused step's outputs).
+    const int Lc = min(max(L_raw, 0), a.max_seq_len);
+    if (p >= max((Lc + kPartition - 1) / kPartition, 1)) return;
+  }
   const int32_t* bt_row = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   auto bt_at = [&](int j) { return bt_row[min(p * 16 + j, a.max_blocks_per_seq - 1)]; };
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -590,14 +605,14 @@ paged_decode_partition_kernel(
           if (a.out16) a.out16[obase[r] + dim] = (uint16_t)bf16_rne_bits(o[c][r]);
           else a.out[obase[r] + dim] = o[c][r];
         }
-        else if constexpr (NTP) __builtin_nontemporal_store(o[c][r], a.part_o + (node + h) * D + dim);
+        else if constexpr (MODE == kRoundsNt) __builtin_nontemporal_store(o[c][r], a.part_o + (node + h) * D + dim);
         else a.part_o[(node + h) * D + dim] = o[c][r];
       }
     }
   }
   if (!direct && tid < rows) {
     float* ml = a.part_ml + (node + tid) * 2;
-    if constexpr (NTP) {
+    if constexpr (MODE == kRoundsNt) {
       __builtin_nontemporal_store(s_M[tid], ml);
       __builtin_nontemporal_store(s_L[tid], ml + 1);
     } else {
@@ -737,20 +752,21 @@ void launch_merge(const DecodeArgs& a, dim3 mgrid, hipStream_t stream) {
 }
 
 // Grids of more workgroups than the chip has CUs (256) run in several
-// rounds; when each workgroup also writes kilobytes of partials, the plain
-// and fused int8 kernels store them with the non-temporal hint (A/B in one
-// process: batch 16 at L ~ U[1K, 32K], 6 KB per workgroup, partition kernel
-// 123.3 -> 119.2 us; 32K call 19.22 -> 18.99 us).  A grid of one round keeps
-// ordinary stores (16K: 9.63 against 9.84 us with the hint), and so do small
-// partials (the MHA batch, 512 B per workgroup: 100.5 against 101.3 us).
-constexpr int64_t kNtPartialsMinGroups = 257;
+// rounds (kRounds).  When each workgroup also writes kilobytes of partials,
+// the plain and fused int8 kernels store them with the non-temporal hint
+// (kRoundsNt; A/B in one process: batch 16 at L ~ U[1K, 32K], 6 KB per
+// workgroup, partition kernel 123.3 -> 119.2 us; 32K call 19.22 -> 18.99 us).
+// A grid of one round keeps ordinary stores (16K: 9.63 against 9.84 us with
+// the hint), and so do small partials (the MHA batch, 512 B per workgroup:
+// 100.5 against 101.3 us).
+constexpr int64_t kRoundsMinGroups = 257;
 constexpr int64_t kNtPartialsMinBytes = 4096;
 
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_seqs == 0) return hipSuccess;
+  const bool rounds = (int64_t)a.max_parts * a.num_kv_heads * a.num_seqs >= kRoundsMinGroups;
   const bool ntp =
-      (int64_t)a.max_parts * a.num_kv_heads * a.num_seqs >= kNtPartialsMinGroups &&
-      (int64_t)a.group * a.nq * a.head_dim * (int64_t)sizeof(float) >= kNtPartialsMinBytes;
+      rounds && (int64_t)a.group * a.nq * a.head_dim * (int64_t)sizeof(float) >= kNtPartialsMinBytes;
   dim3 grid((unsigned)a.max_parts, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
   dim3 mgrid((unsigned)(a.num_q_heads * a.nq), (unsigned)a.num_seqs, (unsigned)(a.head_dim / 32));
 #define I8KV_DECODE_CASE(DD, GG)                                                                 \
@@ -762,7 +778,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
       return hipGetLastError();                                                                  \
     }                                                                                            \
     if (a.new_key && ntp)                                                                        \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8, false, false, true>), \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8, false, false, kRoundsNt>), \
+                         grid, blk, 0, stream, a);                                               \
+    else if (a.new_key && rounds)                                                                \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8, false, false, kRounds>), \
                          grid, blk, 0, stream, a);                                               \
     else if (a.new_key)                                                                          \
       hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, true, kPvInt8, false, false>),   \
@@ -786,7 +805,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, true, false>),   \
                          grid, blk, 0, stream, a);                                               \
     else if (ntp)                                                                                \
-      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false, false, true>), \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false, false, kRoundsNt>), \
+                         grid, blk, 0, stream, a);                                               \
+    else if (rounds)                                                                             \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false, false, kRounds>), \
                          grid, blk, 0, stream, a);                                               \
     else                                                                                         \
       hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, false, false>),  \
