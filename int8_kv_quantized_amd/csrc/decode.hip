@@ -801,6 +801,9 @@ hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream) {
     else if (a.w_uint8)                                                                          \
       hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvUint8, false, false>), \
                          grid, blk, 0, stream, a);                                               \
+    else if (mq && rounds)                                                                       \
+      hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, true, false, kRounds>), \
+                         grid, blk, 0, stream, a);                                               \
     else if (mq)                                                                                 \
       hipLaunchKernelGGL((paged_decode_partition_kernel<DD, GG, false, kPvInt8, true, false>),   \
                          grid, blk, 0, stream, a);                                               \
