@@ -81,6 +81,12 @@ CASES = [
     # 6 KB of partials per workgroup (the non-temporal-store instantiations)
     dict(name="step_d256_g6_rounds", seq_lens=(20000, 1, 9000, 31000, 257), num_q_heads=24,
          num_kv_heads=4, head_dim=256),
+    # 9 partitions x 2 KV heads x 40 sequences of seeded lengths: several rounds
+    # with 1 KB of partials per workgroup (the several-rounds instantiation
+    # without the non-temporal stores); most workgroups lie past their sequence
+    dict(name="step_d128_g2_rounds",
+         seq_lens=tuple(int(x) for x in np.random.default_rng(74).integers(1, 2200, 40)),
+         num_q_heads=4, num_kv_heads=2, head_dim=128),
 ]
 
 
