@@ -133,6 +133,24 @@ def test_decode_many_sequences(orc):
     run_decode(wl, orc, 32, report=False)
 
 
+@pytest.mark.parametrize("G", [32, 64])
+@pytest.mark.parametrize("shape", [(4, 2, 64), (8, 4, 256), (12, 4, 256)],
+                         ids=["d64_g2", "d256_g2", "d256_g3"])
+def test_decode_batch_of_rounds(orc, shape, G):
+    """Grids of several rounds for every head size (60 sequences of seeded
+    lengths 1 .. 3000, so most partition workgroups lie past their sequence
+    and leave on the length): D = 64 and 256 with partials under 4 KB per
+    workgroup (ordinary stores), and D = 256 with three heads per KV head."""
+    Hq, Hkv, D = shape
+    rng = np.random.default_rng(73)
+    lens = rng.integers(1, 3001, 60)
+    wl = W.make_workload(f"rounds_{Hq}_{Hkv}_{D}", seq_lens=tuple(int(x) for x in lens),
+                         new_tokens=[1] * lens.size, num_q_heads=Hq, num_kv_heads=Hkv,
+                         head_dim=D, seed=73, w_group=G)
+    assert ((int(lens.max()) + 255) // 256) * Hkv * lens.size > 256
+    run_decode(wl, orc, G, report=False)
+
+
 def test_decode_long_sequences_many_merge_rounds(orc):
     """150001 and 70000 tokens: 586 and 274 partitions, so the merge runs
     ten and five rounds of 64 partitions, with ragged last partitions."""
