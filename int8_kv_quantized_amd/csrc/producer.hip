@@ -20,7 +20,9 @@
 //
 // With positions given, Q and K are first turned by the rotary embedding of
 // their token's position (section 2.2 lists RoPE inside the producer): the
-// rotate-half pairing of rope_wave_vector, from a caller-given cos | sin table.
+// rotate-half pairing, from a caller-given cos | sin table -- rope_wave_vector
+// over the first rotary_dim < D dims, rope_wave_vector_full (table rows
+// prefetched, pairs exchanged by v_permlane32_swap) over the whole head.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
