@@ -626,11 +626,11 @@ paged_decode_partition_kernel(
 //   O = sum_p w_p o_p / sum_p w_p, w_p = l_p exp(m_p - M), M = max_p m_p.
 // Lane l owns float4 column l % 8 of the 32-dim slice for partitions
 // p = l / 8 (mod 8), U per round (RP = 8 U partitions per round: 64, or 128
-// when the call has more than 64); the partial loads of the first round and
-// the (m, l) of partitions l, l + 64, ... of the first round go out before the
-// sequence length is known (every slot below max_parts exists in the
-// workspace; slots past the sequence are discarded), so a sequence of up to
-// RP partitions costs one memory round trip.  The weight of partition p is
+// when the call has more than 64); for a single sequence the partial loads of
+// the first round and the (m, l) of partitions l, l + 64, ... of the first
+// round go out before the sequence length is known (every slot below
+// max_parts exists in the workspace; slots past the sequence are discarded),
+// so a sequence of up to RP partitions costs one memory round trip.  The weight of partition p is
 // computed by lane p % 64 and fetched with a cross-lane read; the eight lane
 // groups are summed with two swaps and one xor exchange.  (32 rather than 64
 // dims per wave: twice the waves, half the loads per lane -- 1% faster at
@@ -652,20 +652,34 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
   const size_t ostride = (size_t)rows * D;
   const float* po = a.part_o + (base * rows + row) * D + 32 * slice + 4 * col;
   float4 v[U];
+  int qlast = a.max_parts - 1;
   auto issue = [&](int q0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int q = min(q0 + lg + 8 * u, a.max_parts - 1);
+      const int q = min(q0 + lg + 8 * u, qlast);
       v[u] = *reinterpret_cast<const float4*>(po + (size_t)q * ostride);
     }
   };
-  issue(0);
   float2 ml0[NML];
+  auto issue_first = [&]() {
+    issue(0);
 #pragma unroll
-  for (int k = 0; k < NML; ++k) ml0[k] = ml[(size_t)min(lane + kWave * k, a.max_parts - 1) * rows];
+    for (int k = 0; k < NML; ++k) ml0[k] = ml[(size_t)min(lane + kWave * k, qlast) * rows];
+  };
+  // One sequence: the first round goes out before its length is known (one
+  // memory round trip).  A batch waits for the length and loads no slot past
+  // its sequence, so that its shorter sequences do not fetch what they drop
+  // (with U = 16: batch 16 at L ~ U[1K, 32K] call 123.6 -> 123.0 us, MHA
+  // batch 8 102.4 -> 101.9 us, A/B in one process).
   int L = a.seq_lens[s];
+  const bool batch = a.num_seqs > 1;
+  if (!batch) issue_first();
   L = min(max(L, 0), a.max_seq_len);
   const int P_s = (L + kPartition - 1) / kPartition;
+  if (batch) {
+    qlast = max(P_s - 1, 0);
+    if (!(a.stage == 0 && P_s <= 1)) issue_first();
+  }
   const size_t o = (((size_t)s * a.nq + qi) * a.num_q_heads + h) * D + 32 * slice;
   auto put4 = [&](float x0, float x1, float x2, float x3) {
     if (a.out16)
@@ -739,13 +753,13 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
   }
 }
 
-// The merge with one round per 64 partitions (U = 8) or per 128 (U = 16).
-// The wider round pays off for one long sequence (32K: 20.4 -> 19.9 us per
-// call); in a batch, sequences shorter than max_parts would load slots they do
-// not have in the first round (batch 16 at L ~ U[1K, 32K]: 132.8 -> 134.1 us).
+// The merge with one round per 64 partitions (U = 8) or per 128 (U = 16),
+// the wider round whenever a sequence may have more than 64 partitions (32K:
+// 20.4 -> 19.9 us per call; in a batch it pays once the first round no longer
+// loads slots past each sequence).
 template <int D>
 void launch_merge(const DecodeArgs& a, dim3 mgrid, hipStream_t stream) {
-  if (a.max_parts > 64 && a.num_seqs == 1)
+  if (a.max_parts > 64)
     hipLaunchKernelGGL((paged_decode_merge_kernel<D, 16>), mgrid, dim3(kWave), 0, stream, a);
   else
     hipLaunchKernelGGL((paged_decode_merge_kernel<D, 8>), mgrid, dim3(kWave), 0, stream, a);
