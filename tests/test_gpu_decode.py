@@ -134,13 +134,15 @@ def test_decode_many_sequences(orc):
 
 
 @pytest.mark.parametrize("G", [32, 64])
-@pytest.mark.parametrize("shape", [(4, 2, 64), (8, 4, 256), (12, 4, 256)],
-                         ids=["d64_g2", "d256_g2", "d256_g3"])
+@pytest.mark.parametrize("shape", [(4, 2, 64), (8, 4, 256), (12, 4, 256), (16, 1, 256)],
+                         ids=["d64_g2", "d256_g2", "d256_g3", "d256_g16"])
 def test_decode_batch_of_rounds(orc, shape, G):
     """Grids of several rounds for every head size (60 sequences of seeded
     lengths 1 .. 3000, so most partition workgroups lie past their sequence
     and leave on the length): D = 64 and 256 with partials under 4 KB per
-    workgroup (ordinary stores), and D = 256 with three heads per KV head."""
+    workgroup (ordinary stores), D = 256 with three heads per KV head (the
+    partials staged in LDS and stored non-temporally), and D = 256 with 16
+    heads per KV head (the largest staged block, 16 rows x 256 dims)."""
     Hq, Hkv, D = shape
     rng = np.random.default_rng(73)
     lens = rng.integers(1, 3001, 60)

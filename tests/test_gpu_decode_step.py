@@ -87,6 +87,12 @@ CASES = [
     dict(name="step_d128_g2_rounds",
          seq_lens=tuple(int(x) for x in np.random.default_rng(74).integers(1, 2200, 40)),
          num_q_heads=4, num_kv_heads=2, head_dim=128),
+    # 16 q heads per KV head at D = 256 over 30 sequences of seeded lengths:
+    # several rounds with the largest staged partials (16 rows x 256 dims)
+    # and the fused quantization of 16 queries per workgroup
+    dict(name="step_d256_g16_rounds",
+         seq_lens=tuple(int(x) for x in np.random.default_rng(75).integers(1, 4000, 30)),
+         num_q_heads=16, num_kv_heads=1, head_dim=256),
 ]
 
 
