@@ -761,6 +761,12 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
       }
       wsum += wl[k];
     }
+    // every weight this lane needs, fetched before any is used (one wait
+    // for all the cross-lane reads instead of one per partition group)
+    float wqs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) wqs[u] = __shfl(wl[(8 * u) / kWave], (lg + 8 * u) % kWave, kWave);
+    __builtin_amdgcn_sched_barrier(0);
     if (q0 > 0) issue(q0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -768,7 +774,7 @@ __global__ __launch_bounds__(kWave) void paged_decode_merge_kernel(DecodeArgs a)
       // known) but never written: whatever they hold, even NaN or Inf, is
       // dropped by the select, not multiplied by a zero weight.
       const bool live = q0 + lg + 8 * u < P_s;
-      const float wq = __shfl(wl[(8 * u) / kWave], (lg + 8 * u) % kWave, kWave);
+      const float wq = wqs[u];
       acc.x += live ? wq * v[u].x : 0.0f;
       acc.y += live ? wq * v[u].y : 0.0f;
       acc.z += live ? wq * v[u].z : 0.0f;
